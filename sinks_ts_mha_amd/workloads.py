@@ -1,0 +1,116 @@
+"""Seeded synthetic workloads for prefill attention: shapes and random draws only.
+
+This module is shared by the HIP tests, the oracle tests and the benchmark.  It
+holds none of the attention arithmetic: it draws inputs and describes shapes.
+
+Shapes follow the GPT-OSS prefill case of "TokenSpeed-kernel multi-silicon"
+(aixai.ru blog), section "Числа: Gluon на AMD MI355X": bf16 Q/K/V, head_dim 64,
+64 query heads over 8 KV heads, full causal, sequence lengths 1K-8K, batch 1-16.
+The windowed workloads use the sliding-window layers named there and in the
+ai-radar.it article, section "AMD MI355X: la prova sul campo".  No dataset or
+trained weights exist for these pages' measurements; N(0, 1) inputs of the same
+shapes stand in for them.
+
+Recipe (identical bits reach the oracle and the GPU):
+  one CPU torch.Generator seeded with `seed` draws, in this order,
+  q [T, Hq, D], k [T, Hkv, D], v [T, Hkv, D], sinks [Hq] as float32 N(0, 1);
+  q, k, v are then rounded to bfloat16 (round to nearest even).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    seqlens: tuple
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int = 64
+    window: int = 0            # <= 0: full causal
+    sinks: bool = True
+    softmax_scale: float = 0.125
+    seed: int = 0
+    notes: str = field(default="", compare=False)
+
+    @property
+    def total_tokens(self) -> int:
+        return int(sum(self.seqlens))
+
+    @property
+    def max_seqlen(self) -> int:
+        return int(max(self.seqlens)) if self.seqlens else 0
+
+    def cu_seqlens(self) -> torch.Tensor:
+        cu = [0]
+        for n in self.seqlens:
+            cu.append(cu[-1] + int(n))
+        return torch.tensor(cu, dtype=torch.int32)
+
+
+def varlen16_lengths(seed: int = 1, n: int = 16, lo: int = 128, hi: int = 8192) -> tuple:
+    """Sequence lengths drawn uniformly from [lo, hi] inclusive by a seeded CPU generator."""
+    g = torch.Generator().manual_seed(seed)
+    return tuple(int(x) for x in torch.randint(lo, hi + 1, (n,), generator=g))
+
+
+WORKLOADS = {
+    "tiny_1x128_gqa4": Workload(
+        "tiny_1x128_gqa4", (128,), 4, 1,
+        notes="1 sequence of 128 tokens, 4 q heads over 1 KV head, full causal, sinks"),
+    "gptoss_full_4x2048": Workload(
+        "gptoss_full_4x2048", (2048,) * 4, 64, 8,
+        notes="GPT-OSS full-causal layer: 4 x 2048 packed, 64 q / 8 KV heads, sinks"),
+    "gptoss_window128_4x2048": Workload(
+        "gptoss_window128_4x2048", (2048,) * 4, 64, 8, window=128,
+        notes="GPT-OSS sliding-window layer: 4 x 2048 packed, window 128, sinks"),
+    "varlen16_window128": Workload(
+        "varlen16_window128", varlen16_lengths(), 64, 8, window=128,
+        notes="16 sequences, lengths uniform in [128, 8192] (seed 1), window 128, sinks"),
+    "long_1x32768": Workload(
+        "long_1x32768", (32768,), 64, 8,
+        notes="1 sequence of 32768 tokens, 64 q / 8 KV heads, full causal, sinks"),
+}
+
+# The workload a benchmark step runs by default: the full-causal GPT-OSS layer.
+DEFAULT_BENCH_WORKLOAD = "gptoss_full_4x2048"
+
+
+def make_inputs(wl: Workload, seed: int | None = None, device: str = "cpu") -> dict:
+    """Draw q, k, v (bf16) and sinks (fp32) for a workload; see the module recipe."""
+    seed = wl.seed if seed is None else seed
+    T, D = wl.total_tokens, wl.head_dim
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((T, wl.n_q_heads, D), generator=g, dtype=torch.float32)
+    k = torch.randn((T, wl.n_kv_heads, D), generator=g, dtype=torch.float32)
+    v = torch.randn((T, wl.n_kv_heads, D), generator=g, dtype=torch.float32)
+    sinks = torch.randn((wl.n_q_heads,), generator=g, dtype=torch.float32)
+    out = {
+        "q": q.to(torch.bfloat16),
+        "k": k.to(torch.bfloat16),
+        "v": v.to(torch.bfloat16),
+        "sinks": sinks if wl.sinks else None,
+        "cu_seqlens": wl.cu_seqlens(),
+        "max_seqlen": wl.max_seqlen,
+        "window": wl.window,
+        "softmax_scale": wl.softmax_scale,
+    }
+    if device != "cpu":
+        out = {key: (val.to(device) if isinstance(val, torch.Tensor) else val)
+               for key, val in out.items()}
+    return out
+
+
+def custom(seqlens, n_q_heads, n_kv_heads, window=0, sinks=True, head_dim=64,
+           softmax_scale=0.125, seed=0, name="custom") -> Workload:
+    return Workload(name, tuple(int(x) for x in seqlens), n_q_heads, n_kv_heads, head_dim,
+                    window, sinks, softmax_scale, seed)
+
+
+def bf16_bits(t: torch.Tensor):
+    """bf16 tensor -> numpy uint16 array of its bit patterns (no rounding)."""
+    assert t.dtype == torch.bfloat16
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view("uint16")
