@@ -1,0 +1,221 @@
+"""Benchmark: prefill attention TFLOP/s (unmasked pairs) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step is one ts_mha_prefill call over the whole workload: every stage of the
+operation (tile walk, QK^T, mask, online softmax with sink, PV, epilogue) runs
+inside that single kernel launch.  Inputs are seeded synthetic tensors already
+resident in device memory when the timed region starts.
+
+Metric: FLOP = 4 * head_dim * n_q_heads * (visible query-key pairs per head),
+i.e. 2*head_dim flops for q.k and 2*head_dim for the weighted sum of v, counted
+only on unmasked pairs.  Printed as one JSON line with a `roofline` object (the
+kernel's average duration from HIP events on the launch stream against the
+bf16 dense MFMA peak) and a `cpu_baseline` object (the fp64 oracle timed on
+this host's cores on a bounded row sample of the same workload).
+
+Only one GPU is used; --gpus above 1 is refused.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA peak
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E bandwidth
+KERNEL_SOURCE = os.path.join(ROOT, "sinks_ts_mha_amd", "csrc", "prefill_fwd.hip")
+METRIC = "prefill attention TFLOP/s (unmasked pairs) and % of MI355X bf16 MFMA peak"
+
+
+def source_sha() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, if it is for this kernel source."""
+    path = os.path.join(ROOT, "profiles", f"pmc_prefill_fwd_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        m = re.match(r"^([A-Za-z0-9_]+):\s*(.+?)\s*$", line)
+        if m:
+            kv[m.group(1)] = m.group(2)
+    if kv.get("source_sha256") != source_sha():
+        return None
+    try:
+        fetch = float(kv["FETCH_SIZE_KiB_per_dispatch"]) * 1024 * float(kv["fetch_scale"])
+        write = float(kv["WRITE_SIZE_KiB_per_dispatch"]) * 1024 * float(kv["write_scale"])
+    except (KeyError, ValueError):
+        return None
+    return fetch + write
+
+
+def algorithmic_bytes(wl) -> int:
+    T, D = wl.total_tokens, wl.head_dim
+    return T * (2 * wl.n_q_heads * D + 2 * wl.n_kv_heads * D) * 2 + 4 * wl.n_q_heads + \
+        4 * (len(wl.seqlens) + 1)
+
+
+def cpu_baseline(wl, inp, target_s: float):
+    """Time the fp64 oracle on a strided row sample sized for about target_s seconds."""
+    import numpy as np
+
+    from oracle import oracle
+    from sinks_ts_mha_amd.workloads import bf16_bits
+
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+    if not os.path.exists(os.path.join(ROOT, "oracle", "libts_oracle.so")):
+        oracle.build()
+    args = (bf16_bits(inp["q"]), bf16_bits(inp["k"]), bf16_bits(inp["v"]),
+            inp["sinks"].numpy() if inp["sinks"] is not None else None,
+            inp["cu_seqlens"].numpy(), inp["window"], inp["softmax_scale"])
+    cu = inp["cu_seqlens"].numpy().astype(np.int64)
+    W = inp["window"]
+    pos_all, tok_all = [], []
+    for b in range(len(cu) - 1):
+        i = np.arange(cu[b + 1] - cu[b])
+        pos_all.append(i)
+        tok_all.append(cu[b] + i)
+    pos_all = np.concatenate(pos_all)
+    tok_all = np.concatenate(tok_all)
+    keys = np.minimum(pos_all + 1, W) if W > 0 else pos_all + 1
+    hq, D = wl.n_q_heads, wl.head_dim
+
+    def run(stride):
+        sel = np.arange(0, tok_all.size, stride)
+        rows = np.repeat(tok_all[sel], hq)
+        heads = np.tile(np.arange(hq, dtype=np.int32), sel.size)
+        t0 = time.perf_counter()
+        oracle.prefill_rows(*args, rows=rows, heads=heads)
+        dt = time.perf_counter() - t0
+        return dt, float(keys[sel].sum()) * hq * 4 * D, sel.size
+
+    # probe with a thin sample, then size the real one for the target time
+    dt, flops, _ = run(max(1, tok_all.size // 64))
+    rate = flops / max(dt, 1e-6)
+    total_flops = float(keys.sum()) * hq * 4 * D
+    stride = max(1, int(round(total_flops / max(rate * target_s, 1.0))))
+    dt, flops, n = run(stride)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"every {stride}th packed token ({n} of {tok_all.size}), all {hq} q heads, "
+                      f"fp64 oracle rows; {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter calibration runs)")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {a.gpus} is not supported "
+              "(the operation shards by KV-head group or by sequence with no exchange, "
+              "so one GPU's throughput is the figure measured here).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sinks_ts_mha_amd as tm
+    from sinks_ts_mha_amd import workloads
+
+    name = a.workload or workloads.DEFAULT_BENCH_WORKLOAD
+    wl = workloads.WORKLOADS[name]
+    inp = workloads.make_inputs(wl)
+    dev = torch.device("cuda", 0)
+    q, k, v = inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev)
+    sinks = inp["sinks"].to(dev) if inp["sinks"] is not None else None
+    cu = inp["cu_seqlens"].to(dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        tm.ts_mha_prefill(q, k, v, sinks, cu, window=wl.window, softmax_scale=wl.softmax_scale,
+                          out=out, max_seqlen=wl.max_seqlen, stream=stream)
+
+    if a.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_ms = sum(durs_ms) / len(durs_ms)
+    ms_per_step = wall * 1e3 / a.steps
+
+    pairs = tm.ts_mha_unmasked_pairs(wl.cu_seqlens(), wl.window)
+    flops = 4 * wl.head_dim * wl.n_q_heads * pairs
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    traffic = read_traffic(name)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q/k/v, fp32 sinks)",
+        "config": {"workload": name, "seqlens": list(wl.seqlens) if len(wl.seqlens) <= 16 else None,
+                   "total_tokens": wl.total_tokens, "n_q_heads": wl.n_q_heads,
+                   "n_kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "window": wl.window,
+                   "sinks": wl.sinks, "softmax_scale": wl.softmax_scale},
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "unmasked_pairs_per_head": pairs,
+        "flops_per_step": flops,
+        "kernel_avg_us": round(avg_ms * 1e3, 2),
+        "kernel_min_us": round(min(durs_ms) * 1e3, 2),
+        "algorithmic_GBps": round(algorithmic_bytes(wl) / (avg_ms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    if wl.window > 0:
+        line["roofline_hbm"] = {"bound": "hbm",
+                                "achieved": round(algorithmic_bytes(wl) / (avg_ms * 1e-3) / 1e9, 1),
+                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": round(algorithmic_bytes(wl) / (avg_ms * 1e-3) / 1e9 /
+                                              PEAK_HBM_GBS, 4)}
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, inp, a.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,136 @@
+"""Thin ctypes binding over libts_mha.so (declared in include/ts_mha.h).
+
+Argument marshalling only: shapes, dtypes and devices of torch tensors are
+checked and turned into the C call's pointers and sizes; every step of the
+attention runs in the library's HIP kernels.  There is no fallback: if the
+library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libts_mha.so")
+
+TS_MHA_OK = 0
+ERROR_NAMES = {
+    -1: "TS_MHA_ERR_NULL_ARG", -2: "TS_MHA_ERR_BAD_SHAPE", -3: "TS_MHA_ERR_UNSUPPORTED",
+    -4: "TS_MHA_ERR_BAD_SCALE", -5: "TS_MHA_ERR_ALIGN", -6: "TS_MHA_ERR_NO_DEVICE",
+    -7: "TS_MHA_ERR_ARCH", -8: "TS_MHA_ERR_LAUNCH", -9: "TS_MHA_ERR_SEQLENS",
+}
+
+_lib = None
+
+
+class TsMhaError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{ERROR_NAMES.get(code, code)}: {message}")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """Load libts_mha.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sinks_ts_mha_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        L.ts_mha_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_float,
+                                     vp, i32, i32, vp]
+        L.ts_mha_prefill.restype = ctypes.c_int
+        L.ts_mha_strerror.argtypes = [ctypes.c_int]
+        L.ts_mha_strerror.restype = ctypes.c_char_p
+        L.ts_mha_unmasked_pairs.argtypes = [ctypes.POINTER(ctypes.c_int32), i32, i32]
+        L.ts_mha_unmasked_pairs.restype = i64
+        _lib = L
+    return _lib
+
+
+def ts_mha_strerror(code: int) -> str:
+    return lib().ts_mha_strerror(int(code)).decode()
+
+
+def ts_mha_unmasked_pairs(cu_seqlens, window: int = 0) -> int:
+    """Visible (query, key) pairs per head for host cu_seqlens (sequence or CPU tensor)."""
+    cu = torch.as_tensor(cu_seqlens, dtype=torch.int32).cpu().contiguous()
+    n = int(cu.numel()) - 1
+    r = lib().ts_mha_unmasked_pairs(ctypes.cast(cu.data_ptr(), ctypes.POINTER(ctypes.c_int32)),
+                                    n, int(window))
+    if r < 0:
+        raise ValueError("ts_mha_unmasked_pairs rejected cu_seqlens")
+    return int(r)
+
+
+def _overlaps(a: torch.Tensor, b: torch.Tensor) -> bool:
+    a0, b0 = a.data_ptr(), b.data_ptr()
+    a1 = a0 + a.numel() * a.element_size()
+    b1 = b0 + b.numel() * b.element_size()
+    return a0 < b1 and b0 < a1 and a.numel() > 0 and b.numel() > 0
+
+
+def ts_mha_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks, cu_seqlens,
+                   window: int = 0, softmax_scale: float | None = None, out=None,
+                   max_seqlen: int | None = None, stream=None) -> torch.Tensor:
+    """Causal GQA prefill attention with optional sinks and sliding window.
+
+    q [T, Hq, 64], k/v [T, Hkv, 64] bf16 CUDA tensors; sinks fp32 [Hq] or None;
+    cu_seqlens int32 [n_seqs + 1] on the same device.  max_seqlen (the longest
+    sequence) sizes the launch; if omitted it is read back from cu_seqlens,
+    which synchronises.  softmax_scale defaults to 1/sqrt(head_dim).  Runs on
+    `stream` (default: torch's current stream) and returns `out`.
+    """
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.dim() != 3:
+            raise TypeError(f"{name} must be a 3-D bfloat16 tensor")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if k.shape != v.shape or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]:
+        raise ValueError("shapes must be q [T, Hq, D], k = v [T, Hkv, D]")
+    dev = q.device
+    if k.device != dev or v.device != dev:
+        raise ValueError("q, k, v must be on one device")
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 \
+            or cu_seqlens.dim() != 1 or cu_seqlens.device != dev or not cu_seqlens.is_contiguous():
+        raise TypeError("cu_seqlens must be a contiguous int32 1-D tensor on q's device")
+    if sinks is not None:
+        if not isinstance(sinks, torch.Tensor) or sinks.dtype != torch.float32 \
+                or sinks.shape != (q.shape[1],) or sinks.device != dev or not sinks.is_contiguous():
+            raise TypeError("sinks must be None or a contiguous float32 [Hq] tensor on q's device")
+    T, hq, D = q.shape
+    hkv = k.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != torch.bfloat16 or out.device != dev \
+            or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q on q's device")
+    for name, t in (("q", q), ("k", k), ("v", v), ("cu_seqlens", cu_seqlens)) + \
+            ((("sinks", sinks),) if sinks is not None else ()):
+        if _overlaps(out, t):
+            raise ValueError(f"out must not overlap {name}")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / (D ** 0.5)
+    if T == 0:  # no rows: nothing to compute or write (torch gives empty tensors no address)
+        return out
+    n_seqs = cu_seqlens.numel() - 1
+    if max_seqlen is None:
+        cu = cu_seqlens.cpu()
+        max_seqlen = int((cu[1:] - cu[:-1]).max()) if n_seqs > 0 else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    rc = lib().ts_mha_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                              None if sinks is None else sinks.data_ptr(),
+                              cu_seqlens.data_ptr(), hq, hkv, D, int(window), float(softmax_scale),
+                              out.data_ptr(), n_seqs, int(max_seqlen), handle)
+    if rc != TS_MHA_OK:
+        raise TsMhaError(rc, ts_mha_strerror(rc))
+    return out
+
+
+# The operation's name in the public API the pages list.
+mha_prefill = ts_mha_prefill

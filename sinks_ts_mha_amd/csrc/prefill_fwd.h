@@ -1,0 +1,32 @@
+// prefill_fwd.h -- internal interface between the C ABI layer and the gfx950
+// prefill attention kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsmha {
+
+struct PrefillArgs {
+  const void* q;             // bf16 [T][n_q_heads][64]
+  const void* k;             // bf16 [T][n_kv_heads][64]
+  const void* v;             // bf16 [T][n_kv_heads][64]
+  const float* sinks;        // fp32 [n_q_heads] or nullptr
+  const int32_t* cu_seqlens; // int32 [n_seqs + 1]
+  void* out;                 // bf16 [T][n_q_heads][64]
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t window;            // <= 0: none
+  float softmax_scale;
+  int32_t n_seqs;
+  int32_t max_seqlen;
+};
+
+// Number of work-groups the launch will use (0 means nothing to launch), or
+// -1 if the grid would not fit the launch limits.
+int64_t prefill_grid_size(const PrefillArgs& a);
+
+// Enqueue the kernel; returns the launch's hipError_t.
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace tsmha

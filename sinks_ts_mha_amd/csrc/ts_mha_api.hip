@@ -1,0 +1,166 @@
+// ts_mha_api.hip -- the C ABI declared in include/ts_mha.h: host-side argument
+// validation, device capability check, error text, and the pair count used by
+// the throughput metric.  All arithmetic of the operation runs in the kernels
+// of prefill_fwd.hip.
+#include "ts_mha.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "prefill_fwd.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Per-device answer to "is this a gfx950?": 0 unknown, 1 yes, 2 no.
+int g_arch_state[kMaxDevices];
+std::mutex g_arch_mutex;
+
+thread_local char g_launch_msg[256] = "";
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_device() {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+    (void)hipGetLastError();
+    return TS_MHA_ERR_NO_DEVICE;
+  }
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return TS_MHA_ERR_NO_DEVICE;
+  }
+  // Test hook: pretend the device reports this architecture name.
+  const char* forced = getenv("TS_MHA_TEST_ARCH");
+  if (forced && forced[0]) return strncmp(forced, "gfx950", 6) == 0 ? TS_MHA_OK : TS_MHA_ERR_ARCH;
+  if (dev >= kMaxDevices) return TS_MHA_ERR_ARCH;
+  std::lock_guard<std::mutex> lock(g_arch_mutex);
+  if (g_arch_state[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return TS_MHA_ERR_NO_DEVICE;
+    }
+    g_arch_state[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+  }
+  return g_arch_state[dev] == 1 ? TS_MHA_OK : TS_MHA_ERR_ARCH;
+}
+
+// Debug mode: read cu_seqlens back and check it against the documented contract.
+int validate_seqlens(const int32_t* cu, int32_t n_seqs, int32_t max_seqlen, hipStream_t stream) {
+  std::vector<int32_t> h((size_t)n_seqs + 1);
+  if (hipMemcpyAsync(h.data(), cu, sizeof(int32_t) * h.size(), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess) {
+    snprintf(g_launch_msg, sizeof g_launch_msg, "%s", hipGetErrorString(hipGetLastError()));
+    return TS_MHA_ERR_LAUNCH;
+  }
+  if (h[0] != 0) return TS_MHA_ERR_SEQLENS;
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    const int64_t len = (int64_t)h[b + 1] - h[b];
+    if (len < 0 || len > max_seqlen) return TS_MHA_ERR_SEQLENS;
+  }
+  return TS_MHA_OK;
+}
+
+}  // namespace
+
+extern "C" int ts_mha_prefill(const void* q, const void* k, const void* v, const float* sinks,
+                              const int32_t* cu_seqlens, int32_t n_q_heads, int32_t n_kv_heads,
+                              int32_t head_dim, int32_t window, float softmax_scale, void* out,
+                              int32_t n_seqs, int32_t max_seqlen, void* stream) {
+  if (!q || !k || !v || !cu_seqlens || !out) return TS_MHA_ERR_NULL_ARG;
+  if (n_q_heads <= 0 || n_kv_heads <= 0 || n_seqs < 0 || max_seqlen < 0) return TS_MHA_ERR_BAD_SHAPE;
+  if (n_q_heads % n_kv_heads != 0) return TS_MHA_ERR_BAD_SHAPE;
+  const int32_t G = n_q_heads / n_kv_heads;
+  if (head_dim != 64) return TS_MHA_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return TS_MHA_ERR_UNSUPPORTED;
+  if (!isfinite(softmax_scale) || !(softmax_scale > 0.f)) return TS_MHA_ERR_BAD_SCALE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(sinks, 4) || !aligned(cu_seqlens, 4))
+    return TS_MHA_ERR_ALIGN;
+
+  tsmha::PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.sinks = sinks;
+  a.cu_seqlens = cu_seqlens;
+  a.out = out;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.window = window;
+  a.softmax_scale = softmax_scale;
+  a.n_seqs = n_seqs;
+  a.max_seqlen = max_seqlen;
+  const int64_t grid = tsmha::prefill_grid_size(a);
+  if (grid < 0) return TS_MHA_ERR_BAD_SHAPE;
+
+  const int dev_rc = check_device();
+  if (dev_rc != TS_MHA_OK) return dev_rc;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const char* dbg = getenv("TS_MHA_VALIDATE");
+  if (dbg && dbg[0] == '1' && n_seqs > 0) {
+    const int rc = validate_seqlens(cu_seqlens, n_seqs, max_seqlen, st);
+    if (rc != TS_MHA_OK) return rc;
+  }
+  if (grid == 0) return TS_MHA_OK;
+
+  const hipError_t err = tsmha::launch_prefill(a, st);
+  if (err != hipSuccess) {
+    snprintf(g_launch_msg, sizeof g_launch_msg, "%s", hipGetErrorString(err));
+    return TS_MHA_ERR_LAUNCH;
+  }
+  return TS_MHA_OK;
+}
+
+extern "C" const char* ts_mha_strerror(int code) {
+  switch (code) {
+    case TS_MHA_OK: return "success";
+    case TS_MHA_ERR_NULL_ARG: return "a required pointer argument is NULL";
+    case TS_MHA_ERR_BAD_SHAPE:
+      return "bad shape: heads must be > 0 with n_q_heads a multiple of n_kv_heads, n_seqs and "
+             "max_seqlen must be >= 0, and the launch grid must fit";
+    case TS_MHA_ERR_UNSUPPORTED:
+      return "unsupported configuration: head_dim must be 64 and n_q_heads / n_kv_heads one of "
+             "1, 2, 4, 8, 16";
+    case TS_MHA_ERR_BAD_SCALE: return "softmax_scale must be finite and > 0";
+    case TS_MHA_ERR_ALIGN:
+      return "misaligned pointer: q, k, v, out need 16-byte alignment, sinks and cu_seqlens 4-byte";
+    case TS_MHA_ERR_NO_DEVICE: return "no HIP device is available";
+    case TS_MHA_ERR_ARCH: return "the current HIP device is not a gfx950 (MI355X-class) GPU";
+    case TS_MHA_ERR_LAUNCH: {
+      static thread_local char msg[320];
+      snprintf(msg, sizeof msg, "HIP launch failed: %s", g_launch_msg);
+      return msg;
+    }
+    case TS_MHA_ERR_SEQLENS:
+      return "cu_seqlens violates its contract (cu[0] == 0, non-decreasing, lengths <= max_seqlen)";
+    default: return "unknown error";
+  }
+}
+
+extern "C" int64_t ts_mha_unmasked_pairs(const int32_t* cu_seqlens_host, int32_t n_seqs, int32_t window) {
+  if (!cu_seqlens_host || n_seqs < 0) return -1;
+  int64_t total = 0;
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    const int64_t L = (int64_t)cu_seqlens_host[b + 1] - cu_seqlens_host[b];
+    if (L < 0) return -1;
+    if (window > 0 && window < L) {
+      const int64_t W = window;
+      total += W * (W + 1) / 2 + (L - W) * W;
+    } else {
+      total += L * (L + 1) / 2;
+    }
+  }
+  return total;
+}

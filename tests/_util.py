@@ -28,3 +28,38 @@ def err_stats(got: np.ndarray, ref: np.ndarray) -> dict:
     return {"max_abs": float(d.max()) if d.size else 0.0,
             "mean_abs": float(d.mean()) if d.size else 0.0,
             "ref_rms": float(np.sqrt((ref.astype(np.float64) ** 2).mean())) if ref.size else 0.0}
+
+
+def run_gpu(inp: dict, out=None, stream=None, window=None) -> torch.Tensor:
+    """Run the HIP path (through the C ABI) on an input dict; returns the GPU output tensor."""
+    import sinks_ts_mha_amd as tm
+    dev = torch.device("cuda", 0)
+    q = inp["q"].to(dev)
+    k = inp["k"].to(dev)
+    v = inp["v"].to(dev)
+    sinks = None if inp["sinks"] is None else inp["sinks"].to(dev)
+    cu = inp["cu_seqlens"].to(dev)
+    return tm.ts_mha_prefill(q, k, v, sinks, cu, window=inp["window"] if window is None else window,
+                             softmax_scale=inp["softmax_scale"], out=out,
+                             max_seqlen=inp["max_seqlen"], stream=stream)
+
+
+def say(msg: str):
+    """Name the case before a GPU step, flushed, so a crash report shows where it was."""
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def rounding_bound(inp: dict, ref, lib=None):
+    """Elementwise error allowance of a bf16-P, fp32-accumulate, bf16-output kernel.
+
+    bf16 keeps 8 significant bits, so round-to-nearest has unit roundoff
+    u = 2^-8.  Rounding each normalised probability to bf16 moves output
+    element d by at most u * sum_j p_j |v_jd| (sink included in the
+    normalisation), and rounding the output adds u |out_d|.  sum_j p_j |v_jd|
+    is the oracle's output for |v| (bf16 |v| is exact).  fp32 accumulation and
+    the online rescaling add relative terms near 2^-20, covered by a factor
+    (1 + 2^-6) and an absolute 1e-6.
+    """
+    from oracle import oracle
+    weighted_abs = oracle.prefill(*oracle_args(dict(inp, v=inp["v"].abs())), lib=lib)
+    return 2.0 ** -8 * (1 + 2.0 ** -6) * (weighted_abs + np.abs(ref)) + 1e-6

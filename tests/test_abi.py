@@ -1,0 +1,131 @@
+"""C-ABI contract checks that need no GPU: exports, validation codes, error text, pair counts."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import sinks_ts_mha_amd as tm
+from sinks_ts_mha_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ts_mha.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ts_mha_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["ts_mha_prefill", "ts_mha_strerror", "ts_mha_unmasked_pairs"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tm.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} is not exported"
+    nm = subprocess.run(["nm", "-D", "--defined-only", _binding.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (ts_mha_\w+)$", nm, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_error_codes_match_header():
+    text = open(HEADER).read()
+    codes = {name: int(val) for name, val in
+             re.findall(r"#define (TS_MHA_ERR_\w+) \((-\d+)\)", text)}
+    assert codes == {v: k for k, v in _binding.ERROR_NAMES.items()}
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every case below is rejected on the host
+
+
+def call(q=FAKE, k=FAKE, v=FAKE, sinks=None, cu=FAKE, hq=64, hkv=8, d=64, window=0,
+         scale=0.125, out=FAKE * 2, n_seqs=4, max_seqlen=2048, stream=None):
+    return tm.lib().ts_mha_prefill(q, k, v, sinks, cu, hq, hkv, d, window, scale, out, n_seqs,
+                                   max_seqlen, stream)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(cu=None), -1),
+    (dict(out=None), -1),
+    (dict(hq=0), -2), (dict(hkv=0), -2), (dict(hq=-8), -2), (dict(hq=12, hkv=8), -2),
+    (dict(n_seqs=-1), -2), (dict(max_seqlen=-5), -2),
+    (dict(max_seqlen=2**31 - 1, n_seqs=2**20), -2),
+    (dict(d=128), -3), (dict(d=32), -3), (dict(hq=24, hkv=8), -3), (dict(hq=64, hkv=2), -3),
+    (dict(scale=0.0), -4), (dict(scale=-0.1), -4), (dict(scale=float("nan")), -4),
+    (dict(scale=float("inf")), -4),
+    (dict(q=FAKE + 8), -5), (dict(k=FAKE + 2), -5), (dict(v=FAKE + 4), -5),
+    (dict(out=FAKE + 12), -5), (dict(sinks=FAKE + 2), -5), (dict(cu=FAKE + 1), -5),
+])
+def test_host_validation_codes(kw, code):
+    assert call(**kw) == code
+
+
+def test_validation_precedes_device_check():
+    # With valid arguments the only remaining failure on a GPU-less host is "no device";
+    # on a GPU host this test is skipped because the call would really launch.
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert call() == -6
+    assert call(window=128, sinks=FAKE) == -6
+    assert call(n_seqs=0, max_seqlen=0) == -6
+
+
+def test_strerror_texts():
+    for code in list(_binding.ERROR_NAMES) + [0]:
+        text = tm.ts_mha_strerror(code)
+        assert text and text != "unknown error"
+    assert tm.ts_mha_strerror(12345) == "unknown error"
+    assert "HIP launch failed" in tm.ts_mha_strerror(-8)
+
+
+def brute_pairs(seqlens, window):
+    n = 0
+    for L in seqlens:
+        for i in range(L):
+            for j in range(i + 1):
+                if window <= 0 or i - j < window:
+                    n += 1
+    return n
+
+
+@pytest.mark.parametrize("seqlens,window", [([5], 0), ([5], 2), ([0, 3, 7], 3), ([1, 1], 1),
+                                            ([10, 20, 30], 0), ([10, 20, 30], 15),
+                                            ([64, 65], 64), ([33], 100), ([], 0)])
+def test_unmasked_pairs_brute_force(seqlens, window):
+    cu = [0]
+    for L in seqlens:
+        cu.append(cu[-1] + L)
+    assert tm.ts_mha_unmasked_pairs(cu, window) == brute_pairs(seqlens, window)
+
+
+def test_unmasked_pairs_workloads():
+    from sinks_ts_mha_amd.workloads import WORKLOADS
+    expect = {"tiny_1x128_gqa4": 8256, "gptoss_full_4x2048": 8392704,
+              "gptoss_window128_4x2048": 1016064, "varlen16_window128": 9900928,
+              "long_1x32768": 536887296}
+    for name, n in expect.items():
+        wl = WORKLOADS[name]
+        assert tm.ts_mha_unmasked_pairs(wl.cu_seqlens(), wl.window) == n
+
+
+def test_unmasked_pairs_rejects_bad_input():
+    L = tm.lib()
+    assert L.ts_mha_unmasked_pairs(None, 1, 0) == -1
+    arr = (ctypes.c_int32 * 3)(0, 5, 3)
+    assert L.ts_mha_unmasked_pairs(arr, 2, 0) == -1
+    assert L.ts_mha_unmasked_pairs(arr, -1, 0) == -1
+
+
+def test_binding_rejects_cpu_tensors():
+    q = torch.zeros(4, 2, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 4], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        tm.ts_mha_prefill(q, q[:, :1].contiguous(), q[:, :1].contiguous(), None, cu, max_seqlen=4)
+    with pytest.raises(TypeError):
+        tm.ts_mha_prefill(q.float(), q, q, None, cu, max_seqlen=4)

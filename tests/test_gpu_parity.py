@@ -1,0 +1,95 @@
+"""HIP path vs the fp64 oracle, element by element, through the C ABI.
+
+Gate (every case): max |gpu - oracle| <= 2e-2 and mean |gpu - oracle| <= 2e-3 on
+the bf16 outputs.  Small cases also pass a tighter elementwise bound derived
+from the kernel's roundings (bf16 probabilities, bf16 output; see
+_util.rounding_bound), which a wrong mask, sink or head mapping would break.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle
+from sinks_ts_mha_amd import workloads
+from _util import err_stats, f64, oracle_args, rounding_bound, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+GATE_MAX, GATE_MEAN = 2e-2, 2e-3
+
+
+def check(got, ref, what, bound=None):
+    st = err_stats(got, ref)
+    print(f"  {what}: max_abs={st['max_abs']:.3e} mean_abs={st['mean_abs']:.3e} "
+          f"ref_rms={st['ref_rms']:.3e}", flush=True)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    assert st["max_abs"] <= GATE_MAX, f"{what}: max abs err {st['max_abs']}"
+    assert st["mean_abs"] <= GATE_MEAN, f"{what}: mean abs err {st['mean_abs']}"
+    if bound is not None:
+        excess = np.abs(got - ref) - bound
+        assert excess.max() <= 0, f"{what}: rounding bound exceeded by {excess.max():.3e}"
+
+
+RAGGED = [1, 63, 64, 65, 200, 517]
+SMALL_CASES = [
+    # (seqlens, Hq, Hkv, window, sinks)
+    (RAGGED, 8, 8, 0, True),       # G = 1
+    (RAGGED, 8, 4, 0, True),       # G = 2
+    (RAGGED, 8, 2, 0, False),      # G = 4
+    (RAGGED, 16, 2, 0, True),      # G = 8
+    (RAGGED, 32, 2, 0, True),      # G = 16
+    (RAGGED, 16, 2, 1, True),
+    (RAGGED, 16, 2, 127, True),
+    (RAGGED, 16, 2, 128, True),
+    (RAGGED, 16, 2, 129, False),
+    (RAGGED, 8, 1, 300, True),
+    ([0, 1, 0, 5, 1, 0, 70], 16, 2, 0, True),
+    ([1000], 64, 8, 0, True),
+    ([777, 1], 32, 2, 64, True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_CASES, ids=[f"c{n}" for n in range(len(SMALL_CASES))])
+def test_small_parity(case, oracle_lib):
+    seqlens, hq, hkv, w, sinks = case
+    wl = workloads.custom(seqlens, hq, hkv, window=w, sinks=sinks, seed=7)
+    inp = workloads.make_inputs(wl)
+    if sinks:
+        inp["sinks"] = inp["sinks"] * 2.0  # wider spread of sink weights
+    say(f"small parity seqlens={seqlens} Hq={hq} Hkv={hkv} W={w} sinks={sinks}")
+    got = f64(run_gpu(inp).cpu())
+    torch.cuda.synchronize()
+    ref = oracle.prefill(*oracle_args(inp), lib=oracle_lib)
+    check(got, ref, f"seqlens={seqlens} G={hq // hkv} W={w}",
+          bound=rounding_bound(inp, ref, oracle_lib))
+
+
+FULL = ["tiny_1x128_gqa4", "gptoss_full_4x2048", "gptoss_window128_4x2048", "varlen16_window128"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_workload_parity_all_rows(name, oracle_lib):
+    """Every output element of the workload, same launch as the benchmark's."""
+    wl = workloads.WORKLOADS[name]
+    inp = workloads.make_inputs(wl)
+    say(f"workload parity {name} T={wl.total_tokens}")
+    got = f64(run_gpu(inp).cpu())
+    torch.cuda.synchronize()
+    ref = oracle.prefill(*oracle_args(inp), lib=oracle_lib)
+    check(got, ref, name)
+
+
+def test_long_prefill_sampled_rows(oracle_lib):
+    """1 x 32768 full causal: rows sampled (the oracle would take far too long on all of them):
+    positions 0..255, the last 64 positions and every 521st position, every query head."""
+    wl = workloads.WORKLOADS["long_1x32768"]
+    inp = workloads.make_inputs(wl)
+    say("long prefill 1x32768 sampled rows")
+    got = f64(run_gpu(inp).cpu())
+    torch.cuda.synchronize()
+    T = wl.total_tokens
+    pos = np.unique(np.concatenate([np.arange(256), np.arange(T - 64, T), np.arange(0, T, 521)]))
+    rows = np.repeat(pos, wl.n_q_heads)
+    heads = np.tile(np.arange(wl.n_q_heads), pos.size)
+    ref = oracle.prefill_rows(*oracle_args(inp), rows=rows, heads=heads, lib=oracle_lib)
+    check(got[rows, heads], ref, "long_1x32768 sampled")

@@ -1,0 +1,209 @@
+"""Targeted GPU probes that the loose parity gate cannot see.
+
+Closed forms at tight tolerance (window edges, sink units, head groups), edge
+shapes, bitwise determinism and packing invariance, full overwrite of the
+output, untouched guard bands, and the device checks of the C ABI.
+"""
+import ctypes
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import sinks_ts_mha_amd as tm
+from oracle import oracle
+from sinks_ts_mha_amd import workloads
+from _util import f64, oracle_args, rounding_bound, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def q_zero_reference(inp):
+    """q = 0: out_i = sum_{j in A_i} v_j / (|A_i| + e^sigma_h) (all logits are 0).
+
+    Every probability of a row is then the same number, so its bf16 rounding is
+    one common relative error (at most u = 2^-8) and the output rounding another:
+    |err| <= 2^-7 |ref| up to fp32 terms.  One key too many or too few moves a
+    row by about 1 / sqrt(|A_i|) relative, far above that.
+    """
+    v = inp["v"].to(torch.float64).numpy()
+    hq, hkv = inp["q"].shape[1], v.shape[1]
+    G = hq // hkv
+    w = inp["window"]
+    cu = inp["cu_seqlens"].tolist()
+    ref = np.zeros(inp["q"].shape)
+    for b in range(len(cu) - 1):
+        s, e = cu[b], cu[b + 1]
+        cs = np.concatenate([np.zeros((1,) + v.shape[1:]), np.cumsum(v[s:e], axis=0)])
+        i = np.arange(e - s)
+        cnt = np.minimum(i + 1, w) if w > 0 else i + 1
+        vsum = cs[i + 1] - cs[i + 1 - cnt]                          # [L, Hkv, D]
+        for h in range(hq):
+            extra = math.exp(float(inp["sinks"][h])) if inp["sinks"] is not None else 0.0
+            ref[s:e, h] = vsum[:, h // G] / (cnt[:, None] + extra)
+    return ref
+
+
+@pytest.mark.parametrize("name,window", [("gptoss_full_4x2048", 0), ("gptoss_window128_4x2048", 128),
+                                         ("gptoss_window128_4x2048", 127),
+                                         ("gptoss_window128_4x2048", 129),
+                                         ("gptoss_window128_4x2048", 1)])
+def test_q_zero_closed_form(name, window):
+    wl = workloads.WORKLOADS[name]
+    inp = workloads.make_inputs(wl)
+    inp["q"] = torch.zeros_like(inp["q"])
+    inp["window"] = window
+    inp["sinks"] = torch.linspace(-3.0, 3.0, wl.n_q_heads)
+    say(f"q=0 closed form {name} W={window}")
+    got = f64(run_gpu(inp).cpu())
+    ref = q_zero_reference(inp)
+    err = np.abs(got - ref)
+    bound = 2.0 ** -7 * (1 + 2.0 ** -6) * np.abs(ref) + 1e-5
+    if not np.all(err <= bound):
+        excess = (err - bound).reshape(-1)
+        cu = inp["cu_seqlens"].tolist()
+        for flat in np.argsort(-excess)[:12]:
+            t, h, d = np.unravel_index(flat, got.shape)
+            b = int(np.searchsorted(cu, t, side="right")) - 1
+            print(f"  token {t} (seq {b} pos {t - cu[b]}) head {h} d {d}: got {got[t, h, d]:.6e} "
+                  f"ref {ref[t, h, d]:.6e} excess {excess[flat]:.3e}", flush=True)
+        bad = (err > bound)
+        print(f"  {bad.sum()} elements over; rows over per head: {bad.any(axis=2).sum(axis=0)}")
+    assert np.all(err <= bound), f"max excess {(err - bound).max():.3e}"
+
+
+@pytest.mark.parametrize("window", [1, 2, 3, 127, 128, 129])
+def test_window_edges_tight(window, oracle_lib):
+    wl = workloads.custom([300, 129, 128, 2], 16, 2, window=window, seed=3)
+    inp = workloads.make_inputs(wl)
+    say(f"window edge W={window}")
+    got = f64(run_gpu(inp).cpu())
+    ref = oracle.prefill(*oracle_args(inp), lib=oracle_lib)
+    assert np.all(np.abs(got - ref) <= rounding_bound(inp, ref, oracle_lib))
+
+
+@pytest.mark.parametrize("sink", [None, 0.0, 4.0, 80.0, -80.0])
+def test_sink_values(sink, oracle_lib):
+    wl = workloads.custom([500, 37], 16, 2, window=0, seed=4)
+    inp = workloads.make_inputs(wl)
+    inp["sinks"] = None if sink is None else torch.full((16,), sink)
+    say(f"sink value {sink}")
+    got = f64(run_gpu(inp).cpu())
+    ref = oracle.prefill(*oracle_args(inp), lib=oracle_lib)
+    assert np.all(np.abs(got - ref) <= rounding_bound(inp, ref, oracle_lib))
+    if sink == 80.0:
+        assert np.max(np.abs(got)) < 1e-6
+
+
+def test_edge_shapes(oracle_lib):
+    for seqlens in ([0], [1], [0, 0], [1, 0, 2, 0], [5]):
+        wl = workloads.custom(seqlens, 8, 1, window=0, seed=5)
+        inp = workloads.make_inputs(wl)
+        say(f"edge shape {seqlens}")
+        got = run_gpu(inp)
+        torch.cuda.synchronize()
+        if wl.total_tokens:
+            ref = oracle.prefill(*oracle_args(inp), lib=oracle_lib)
+            assert np.all(np.abs(f64(got.cpu()) - ref) <= rounding_bound(inp, ref, oracle_lib))
+
+
+def test_no_sequences_is_noop():
+    """n_seqs = 0 (and max_seqlen = 0) is accepted and launches nothing."""
+    q = torch.zeros(16, 8, 64, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(16, 1, 64, dtype=torch.bfloat16, device="cuda")
+    out = torch.full_like(q, 3.0)
+    cu = torch.zeros(1, dtype=torch.int32, device="cuda")
+    say("n_seqs = 0")
+    for max_len in (0, 16):
+        rc = tm.lib().ts_mha_prefill(q.data_ptr(), k.data_ptr(), k.data_ptr(), None, cu.data_ptr(),
+                                     8, 1, 64, 0, 0.125, out.data_ptr(), 0, max_len, None)
+        assert rc == 0
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0)
+
+
+def test_packed_equals_alone_bitwise():
+    wl = workloads.custom([70, 1, 300, 129, 0, 64], 16, 2, window=100, seed=6)
+    inp = workloads.make_inputs(wl)
+    say("packed vs alone")
+    packed = run_gpu(inp).cpu()
+    cu = inp["cu_seqlens"].tolist()
+    for b in range(len(cu) - 1):
+        s, e = cu[b], cu[b + 1]
+        if e == s:
+            continue
+        one = dict(inp, q=inp["q"][s:e], k=inp["k"][s:e], v=inp["v"][s:e],
+                   cu_seqlens=torch.tensor([0, e - s], dtype=torch.int32), max_seqlen=e - s)
+        alone = run_gpu(one).cpu()
+        assert torch.equal(alone.view(torch.int16), packed[s:e].view(torch.int16)), f"sequence {b}"
+
+
+def test_deterministic_bitwise():
+    wl = workloads.WORKLOADS["gptoss_full_4x2048"]
+    inp = workloads.make_inputs(wl)
+    say("determinism")
+    a = run_gpu(inp).cpu()
+    b = run_gpu(inp).cpu()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_window_covering_equals_full_bitwise():
+    wl = workloads.custom([1000, 333], 16, 2, window=0, seed=8)
+    inp = workloads.make_inputs(wl)
+    say("window >= length vs full")
+    full = run_gpu(inp).cpu()
+    for w in (1000, 5000):
+        got = run_gpu(inp, window=w).cpu()
+        assert torch.equal(got.view(torch.int16), full.view(torch.int16)), f"W={w}"
+
+
+def test_output_fully_overwritten_and_guards_intact():
+    wl = workloads.custom([257, 3, 1024], 16, 2, window=0, seed=9)
+    inp = workloads.make_inputs(wl)
+    n = inp["q"].numel()
+    guard = 4096
+    buf = torch.full((n + 2 * guard,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out = buf[guard:guard + n].view(inp["q"].shape)
+    say("NaN-poisoned output with guard bands")
+    run_gpu(inp, out=out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any(), "some output element was not written"
+    assert torch.isnan(buf[:guard]).all() and torch.isnan(buf[guard + n:]).all(), "guard band written"
+
+
+def test_runs_on_a_side_stream(oracle_lib):
+    wl = workloads.custom([300, 40], 16, 2, window=0, seed=11)
+    inp = workloads.make_inputs(wl)
+    say("side stream")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        got = run_gpu(inp, stream=s)
+    s.synchronize()
+    ref = oracle.prefill(*oracle_args(inp), lib=oracle_lib)
+    assert np.all(np.abs(f64(got.cpu()) - ref) <= rounding_bound(inp, ref, oracle_lib))
+
+
+def test_arch_check_hook(monkeypatch):
+    q = torch.zeros(4, 8, 64, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(4, 1, 64, dtype=torch.bfloat16, device="cuda")
+    cu = torch.tensor([0, 4], dtype=torch.int32, device="cuda")
+    monkeypatch.setenv("TS_MHA_TEST_ARCH", "gfx942")
+    say("arch hook")
+    with pytest.raises(tm.TsMhaError) as ei:
+        tm.ts_mha_prefill(q, k, k.clone(), None, cu, max_seqlen=4)
+    assert ei.value.code == -7
+
+
+def test_debug_seqlens_validation(monkeypatch):
+    q = torch.zeros(8, 8, 64, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(8, 1, 64, dtype=torch.bfloat16, device="cuda")
+    cu = torch.tensor([0, 3, 8], dtype=torch.int32, device="cuda")
+    monkeypatch.setenv("TS_MHA_VALIDATE", "1")
+    say("debug cu_seqlens validation")
+    with pytest.raises(tm.TsMhaError) as ei:
+        tm.ts_mha_prefill(q, k, k.clone(), None, cu, max_seqlen=4)   # length 5 > 4
+    assert ei.value.code == -9
+    tm.ts_mha_prefill(q, k, k.clone(), None, cu, max_seqlen=5)
+    torch.cuda.synchronize()
