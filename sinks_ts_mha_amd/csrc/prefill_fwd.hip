@@ -29,34 +29,51 @@
 // on the V side), and V^T is read from the row-major V tile with the gfx950
 // LDS transpose read ds_read_b64_tr_b16.
 //
-// Softmax.  Online (streaming) softmax in base 2: t = s * scale * log2(e); the
-// running maximum starts at the sink's logit (times log2 e) so the sink takes
-// part in the maximum and the denominator, and the sink's own term
-// exp2(sigma - m) is added to the denominator once, at the end.  A row whose
-// keys are all masked in a tile uses 0 as its reference so no inf - inf occurs.
+// Staging.  K and V tiles move from HBM straight into LDS with
+// buffer_load_dwordx4 ... lds (no register round trip), double-buffered: the
+// loads of tile t+1 are in flight while tile t is consumed, and one barrier per
+// tile separates the two.  The buffer descriptor of each work-group spans only
+// its own sequence, so rows past the sequence end read as zeros.  Each lane
+// picks its source chunk so that the fixed lane-to-LDS order of these loads
+// lands in the XOR-swizzled layout the readers expect.
+//
+// Softmax.  Online (streaming) softmax in base 2: t = s * scale * log2(e).  The
+// reference maximum of each row starts at the sink's logit (times log2 e), so
+// the sink takes part in the maximum, and the sink's own term exp2(sigma - m)
+// is added to the denominator once, at the end.  The reference is raised only
+// when a tile's row maximum exceeds it by more than 8 (a factor 256), so the
+// rescaling of the accumulators is rare; probabilities stay below 2^8 and fp32
+// sums cannot overflow.  Row sums are taken on the bf16-rounded probabilities
+// (v_dot2c_f32_bf16 against ones), the same values the PV product uses.  A row
+// with no visible key so far uses 0 as its reference, so no inf - inf occurs.
 #include "prefill_fwd.h"
 
 #include <math.h>
 
 namespace tsmha {
-namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kD = 64;                 // head_dim
-constexpr int kBK = 64;                // keys per LDS tile
+constexpr int kD = 64;                        // head_dim
+constexpr int kBK = 64;                       // keys per LDS tile
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRows = 64 * kWaves;     // (query head, position) rows per work-group
-constexpr int kChunksPerRow = kD * 2 / 16;   // 16-byte chunks in one K or V row
+constexpr int kRows = 64 * kWaves;            // (query head, position) rows per work-group
+constexpr int kRowBytes = kD * 2;             // one K or V row in bytes
+constexpr int kChunks = kRowBytes / 16;       // 16-byte chunks per row
+constexpr int kTileChunks = kBK * kChunks;    // 16-byte chunks per tile
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleSlack = 8.f;          // log2 units the reference max may lag by
+constexpr int kBufferConfig = 0x00020000;     // raw buffer descriptor word 3 (32-bit data)
 
 struct KParams {
   const uint16_t* q;
@@ -72,15 +89,42 @@ struct KParams {
   float c;  // softmax_scale * log2(e)
 };
 
-// Swizzled position of 16-byte chunk `ch` of tile row `row`: XOR with the row's
+namespace {
+
+// Position of 16-byte chunk `ch` of tile row `row` in LDS: XOR with the row's
 // low three bits spreads the 8 chunks of 8 consecutive rows over all banks.
-__device__ __forceinline__ int swz(int row, int ch) { return row * kChunksPerRow + (ch ^ (row & 7)); }
+__device__ __forceinline__ int swz(int row, int ch) { return row * kChunks + (ch ^ (row & 7)); }
+
+// max / sum of x over the lane pair (l, l ^ 32): v_permlane32_swap hands each
+// lane both halves of the pair.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// Maximum of 32 values: two independent chains of 3-input maxima (v_max3_f32).
+__device__ __forceinline__ float max32(const f32x16& a, const f32x16& b) {
+  float x = fmaxf(fmaxf(a[0], a[1]), a[2]);
+  float y = fmaxf(fmaxf(b[0], b[1]), b[2]);
+#pragma unroll
+  for (int i = 3; i < 15; i += 2) {
+    x = fmaxf(fmaxf(x, a[i]), a[i + 1]);
+    y = fmaxf(fmaxf(y, b[i]), b[i + 1]);
+  }
+  return fmaxf(fmaxf(x, a[15]), fmaxf(y, b[15]));
+}
+
+}  // namespace
 
 template <int G, bool WINDOWED>
 __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   constexpr int P = kRows / G;  // positions per work-group
-  __shared__ u32x4 lds_k[kBK * kChunksPerRow];
-  __shared__ u32x4 lds_v[kBK * kChunksPerRow];
+  __shared__ u32x4 lds_k[2 * kTileChunks];
+  __shared__ u32x4 lds_v[2 * kTileChunks];
 
   const int Hkv = p.n_kv_heads;
   const int Hq = Hkv * G;
@@ -109,10 +153,37 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   const int kt0 = first / kBK;
   const int kt1 = last / kBK;
 
+  // ---- K/V staging: wave w fills LDS chunks [128 w, 128 w + 128) of each tile,
+  // two wave-wide loads of 64 chunks; lane order is fixed by the hardware, so
+  // each lane fetches the data chunk that belongs at its swizzled position.
+  const int64_t seq_elems = (int64_t)s * Hkv * kD;
+  const int nbytes = L * Hkv * kRowBytes;  // the sequence's K (or V) rows
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + seq_elems), (short)0, nbytes, kBufferConfig);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + seq_elems), (short)0, nbytes, kBufferConfig);
+  int voff[2];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int row = (2 * w + it) * 8 + (lane >> 3);
+    const int data_ch = (lane & 7) ^ (row & 7);
+    voff[it] = (row * Hkv + g) * kRowBytes + data_ch * 16;
+  }
+  auto issue_tile = [&](int kt, int buf) {
+    const int soff = kt * kBK * Hkv * kRowBytes;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int dst = buf * kTileChunks + (2 * w + it) * 64;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)&lds_k[dst], 16, voff[it], soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)&lds_v[dst], 16, voff[it], soff, 0, 0);
+    }
+  };
+  issue_tile(kt0, 0);
+
   // ---- this lane's two query rows (one per 32-column block nb)
   int pos[2], head[2];
   bf16x8 qf[2][4];
-  float m[2], lsum[2];
+  float mref[2], lsum[2];
   f32x16 o[2][2];  // [d block][nb]: O^T, rows = head_dim, columns = queries
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
@@ -128,7 +199,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) qf[nb][ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
     }
-    m[nb] = p.sinks ? p.sinks[head[nb]] * kLog2e : -INFINITY;
+    mref[nb] = p.sinks ? p.sinks[head[nb]] * kLog2e : -INFINITY;
     lsum[nb] = 0.f;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
@@ -136,44 +207,17 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
       for (int e = 0; e < 16; ++e) o[db][nb][e] = 0.f;
   }
 
-  // ---- K/V tile staging: each thread moves 2 chunks of K and 2 of V
-  u32x4 kreg[2], vreg[2];
-  auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int c = tid + kThreads * it;
-      const int row = c / kChunksPerRow, ch = c % kChunksPerRow;
-      const int j = kt * kBK + row;
-      if (j < L) {
-        const int64_t off = ((int64_t)(s + j) * Hkv + g) * kD + ch * 8;
-        kreg[it] = *(const u32x4*)(p.k + off);
-        vreg[it] = *(const u32x4*)(p.v + off);
-      } else {  // past the sequence end: zeros keep the masked products finite
-        kreg[it] = u32x4{0, 0, 0, 0};
-        vreg[it] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int c = tid + kThreads * it;
-      const int row = c / kChunksPerRow, ch = c % kChunksPerRow;
-      lds_k[swz(row, ch)] = kreg[it];
-      lds_v[swz(row, ch)] = vreg[it];
-    }
-  };
-
   const int r16 = lane & 15;
   const int half16 = (lane >> 4) & 1;
-  lds_char* vbase = (lds_char*)(lds_v);
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 
-  load_tile(kt0);
   for (int kt = kt0; kt <= kt1; ++kt) {
-    __syncthreads();  // all waves are done reading the previous tile
-    store_tile();
-    __syncthreads();
-    if (kt < kt1) load_tile(kt + 1);  // in flight while this tile is consumed
+    const int buf = (kt - kt0) & 1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads have landed in LDS
+    __syncthreads();                     // every wave's have; tile kt-1 is fully consumed
+    if (kt < kt1) issue_tile(kt + 1, buf ^ 1);
+    const u32x4* kt_lds = &lds_k[buf * kTileChunks];
+    lds_char* vbase = (lds_char*)&lds_v[buf * kTileChunks];
 
     // ---- S^T = K Q^T for 64 keys x this wave's 64 queries
     f32x16 sacc[2][2];
@@ -188,7 +232,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const int key = 32 * mb + l32;
-        const bf16x8 a = __builtin_bit_cast(bf16x8, lds_k[swz(key, 2 * ks + hi)]);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, kt_lds[swz(key, 2 * ks + hi)]);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
           sacc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[nb][ks], sacc[mb][nb], 0, 0, 0);
@@ -212,40 +256,43 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
           }
     }
 
-    // ---- online softmax; P^T converted to bf16 in the PV B-operand order
+    // ---- raise the reference maxima only when a row outgrows them by > 2^8
+    float mcand[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) mcand[nb] = pair_max(max32(sacc[0][nb], sacc[1][nb])) * p.c;
+    const bool grow = (mcand[0] > mref[0] + kRescaleSlack) || (mcand[1] > mref[1] + kRescaleSlack);
+    if (__any(grow)) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const float mnew = fmaxf(mref[nb], mcand[nb]);
+        const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mref[nb] - mnew);
+        lsum[nb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[db][nb][e] *= alpha;
+        mref[nb] = mnew;
+      }
+    }
+
+    // ---- probabilities, bf16 P^T in the PV B-operand order, row sums of the bf16 values
     bf16x8 pf[4][2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      float mx = -INFINITY;
+      const float muse = (mref[nb] == -INFINITY) ? 0.f : mref[nb];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[mb][nb][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[nb], mx * p.c);
-      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f(m[nb] - muse);
-      float rs = 0.f;
+        for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+          for (int e = 0; e < 8; ++e)
+            pf[2 * mb + h2][nb][e] =
+                (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[mb][nb][8 * h2 + e], p.c, -muse));
+          const bf16x8 v8 = pf[2 * mb + h2][nb];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[mb][nb][e], p.c, -muse));
-          sacc[mb][nb][e] = pe;
-          rs += pe;
+          for (int e = 0; e < 4; ++e)
+            lsum[nb] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v8[2 * e], v8[2 * e + 1]}, ones, lsum[nb], false);
         }
-      lsum[nb] = lsum[nb] * alpha + rs;
-      m[nb] = mnew;
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[db][nb][e] *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pf[2 * mb + h2][nb][e] = (__bf16)sacc[mb][nb][8 * h2 + e];
     }
 
     // ---- O^T += V^T P^T; lane l of step s4 needs keys 16 s4 + 8 (e / 4) + 4 hi + e % 4
@@ -256,8 +303,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
         const int d = 32 * db + 16 * half16 + 4 * (r16 & 3);
-        const int off_lo = key_lo * (kD * 2) + (((d >> 3) ^ (key_lo & 7)) << 4) + (d & 7) * 2;
-        const int off_hi = key_hi * (kD * 2) + (((d >> 3) ^ (key_hi & 7)) << 4) + (d & 7) * 2;
+        const int off_lo = key_lo * kRowBytes + (((d >> 3) ^ (key_lo & 7)) << 4) + (d & 7) * 2;
+        const int off_hi = key_hi * kRowBytes + (((d >> 3) ^ (key_hi & 7)) << 4) + (d & 7) * 2;
         const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + off_lo));
         const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + off_hi));
         const u32x2 u0 = __builtin_bit_cast(u32x2, t0);
@@ -273,8 +320,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   // ---- epilogue: combine the two half-sums, add the sink's term, normalise, store
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    float lt = lsum[nb] + __shfl_xor(lsum[nb], 32);
-    if (p.sinks) lt += __builtin_amdgcn_exp2f(p.sinks[head[nb]] * kLog2e - m[nb]);
+    float lt = pair_sum(lsum[nb]);
+    if (p.sinks) lt += __builtin_amdgcn_exp2f(p.sinks[head[nb]] * kLog2e - mref[nb]);
     const float inv = 1.f / lt;
     if (pos[nb] < L) {
       uint16_t* orow = p.out + ((int64_t)(s + pos[nb]) * Hq + head[nb]) * kD;
@@ -291,6 +338,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
     }
   }
 }
+
+namespace {
 
 template <int G>
 hipError_t launch_group(const KParams& kp, int64_t grid, bool windowed, hipStream_t stream) {
@@ -310,6 +359,8 @@ int64_t pblocks(const PrefillArgs& a) {
 }  // namespace
 
 int64_t prefill_grid_size(const PrefillArgs& a) {
+  // each sequence's K (or V) rows must be addressable by one buffer descriptor
+  if (((int64_t)a.max_seqlen + kBK) * a.n_kv_heads * kRowBytes > 0x7fffffffLL) return -1;
   const int64_t n = pblocks(a) * (int64_t)a.n_seqs * (int64_t)a.n_kv_heads;
   if (n > 0x7fffffffLL) return -1;
   return n;
