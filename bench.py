@@ -36,8 +36,12 @@ METRIC = "prefill attention TFLOP/s (unmasked pairs) and % of MI355X bf16 MFMA p
 
 
 def source_sha() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """Hash of the kernel source's code: comments and whitespace do not count."""
+    text = open(KERNEL_SOURCE).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()
 
 
 def read_traffic(workload: str):

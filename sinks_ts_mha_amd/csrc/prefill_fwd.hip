@@ -35,7 +35,8 @@
 // tile separates the two.  The buffer descriptor of each work-group spans only
 // its own sequence, so rows past the sequence end read as zeros.  Each lane
 // picks its source chunk so that the fixed lane-to-LDS order of these loads
-// lands in the XOR-swizzled layout the readers expect.
+// lands in the XOR-swizzled layout the readers expect.  The XOR pattern is laid
+// out for an LDS that serves 256 bytes (64 banks) per cycle.
 //
 // Softmax.  Online (streaming) softmax in base 2: t = s * scale * log2(e).  The
 // reference maximum of each row starts at the sink's logit (times log2 e), so
@@ -43,9 +44,11 @@
 // is added to the denominator once, at the end.  The reference is raised only
 // when a tile's row maximum exceeds it by more than 8 (a factor 256), so the
 // rescaling of the accumulators is rare; probabilities stay below 2^8 and fp32
-// sums cannot overflow.  Row sums are taken on the bf16-rounded probabilities
-// (v_dot2c_f32_bf16 against ones), the same values the PV product uses.  A row
-// with no visible key so far uses 0 as its reference, so no inf - inf occurs.
+// sums cannot overflow.  Row sums are plain fp32 adds of the probabilities in
+// four independent chains (the packed bf16 dot instruction would halve their
+// count, but on gfx950 it shares the matrix pipeline and waits behind MFMAs of
+// the other wave on the SIMD).  A row with no visible key so far uses 0 as its
+// reference, so no inf - inf occurs.
 #include "prefill_fwd.h"
 
 #include <math.h>
@@ -59,6 +62,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -71,9 +75,12 @@ constexpr int kRows = 64 * kWaves;            // (query head, position) rows per
 constexpr int kRowBytes = kD * 2;             // one K or V row in bytes
 constexpr int kChunks = kRowBytes / 16;       // 16-byte chunks per row
 constexpr int kTileChunks = kBK * kChunks;    // 16-byte chunks per tile
+constexpr int kTileBytes = kTileChunks * 16;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.f;          // log2 units the reference max may lag by
 constexpr int kBufferConfig = 0x00020000;     // raw buffer descriptor word 3 (32-bit data)
+constexpr int kSlots = 2;                     // LDS buffers for K and for V tiles
+
 
 struct KParams {
   const uint16_t* q;
@@ -91,9 +98,14 @@ struct KParams {
 
 namespace {
 
-// Position of 16-byte chunk `ch` of tile row `row` in LDS: XOR with the row's
-// low three bits spreads the 8 chunks of 8 consecutive rows over all banks.
-__device__ __forceinline__ int swz(int row, int ch) { return row * kChunks + (ch ^ (row & 7)); }
+// Position of 16-byte chunk `ch` of tile row `row` in LDS.  The LDS serves 256
+// bytes (64 banks of 4 bytes) per cycle, i.e. two 128-byte tile rows, so rows of
+// equal parity collide unless their chunks differ.  The XOR key uses row bits 1
+// (as chunk bit 2) and 2..3 (as chunk bits 0..1): 16 consecutive rows reading
+// one logical chunk (the K operand reads) and 4 consecutive rows reading 4
+// adjacent chunks (the V transpose reads) both hit 16 distinct bank groups.
+__device__ __forceinline__ int swz_key(int row) { return ((row & 2) << 1) | ((row >> 2) & 3); }
+__device__ __forceinline__ int swz(int row, int ch) { return row * kChunks + (ch ^ swz_key(row)); }
 
 // max / sum of x over the lane pair (l, l ^ 32): v_permlane32_swap hands each
 // lane both halves of the pair.
@@ -118,13 +130,54 @@ __device__ __forceinline__ float max32(const f32x16& a, const f32x16& b) {
   return fmaxf(fmaxf(x, a[15]), fmaxf(y, b[15]));
 }
 
+// Raw buffer descriptor (base, stride 0, byte range n) in scalar registers.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, int n) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(n);
+  r[3] = kBufferConfig;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const u32x4* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)p);
+}
+
+// One wave-wide 16-byte-per-lane load from a buffer straight into LDS: lane i's
+// 16 bytes land at lds + 16 i (lds must be wave-uniform).  Written as inline
+// assembly so that the compiler does not treat later LDS reads of other ring
+// slots as possibly overwritten by this load and stall them on its completion;
+// the kernel orders these loads itself (wait_vmem + barrier).  M0 carries the
+// LDS address and is used by nothing else in these kernels.
+__device__ __forceinline__ void lds_dma16(uint32_t lds, const i32x4& rsrc, int voffset) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voffset), "s"(rsrc)
+      : "m0");
+#pragma clang diagnostic pop
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N <= 15, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
 }  // namespace
 
 template <int G, bool WINDOWED>
 __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   constexpr int P = kRows / G;  // positions per work-group
-  __shared__ u32x4 lds_k[2 * kTileChunks];
-  __shared__ u32x4 lds_v[2 * kTileChunks];
+  __shared__ u32x4 lds_k[kSlots * kTileChunks];
+  __shared__ u32x4 lds_v[kSlots * kTileChunks];
 
   const int Hkv = p.n_kv_heads;
   const int Hq = Hkv * G;
@@ -153,33 +206,6 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   const int kt0 = first / kBK;
   const int kt1 = last / kBK;
 
-  // ---- K/V staging: wave w fills LDS chunks [128 w, 128 w + 128) of each tile,
-  // two wave-wide loads of 64 chunks; lane order is fixed by the hardware, so
-  // each lane fetches the data chunk that belongs at its swizzled position.
-  const int64_t seq_elems = (int64_t)s * Hkv * kD;
-  const int nbytes = L * Hkv * kRowBytes;  // the sequence's K (or V) rows
-  const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + seq_elems), (short)0, nbytes, kBufferConfig);
-  const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + seq_elems), (short)0, nbytes, kBufferConfig);
-  int voff[2];
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int row = (2 * w + it) * 8 + (lane >> 3);
-    const int data_ch = (lane & 7) ^ (row & 7);
-    voff[it] = (row * Hkv + g) * kRowBytes + data_ch * 16;
-  }
-  auto issue_tile = [&](int kt, int buf) {
-    const int soff = kt * kBK * Hkv * kRowBytes;
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int dst = buf * kTileChunks + (2 * w + it) * 64;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)&lds_k[dst], 16, voff[it], soff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)&lds_v[dst], 16, voff[it], soff, 0, 0);
-    }
-  };
-  issue_tile(kt0, 0);
-
   // ---- this lane's two query rows (one per 32-column block nb)
   int pos[2], head[2];
   bf16x8 qf[2][4];
@@ -207,17 +233,47 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
       for (int e = 0; e < 16; ++e) o[db][nb][e] = 0.f;
   }
 
+  // ---- K/V staging, double-buffered: tile t lives in slot (t - kt0) mod 2.
+  // The loads of tile t + 1 are issued right after the barrier that opens tile
+  // t and land while tile t is consumed.  Wave w fills LDS chunks
+  // [128 w, 128 w + 128) of a tile with two wave-wide loads; the lane-to-LDS
+  // order is fixed by the hardware, so each lane fetches the data chunk that
+  // belongs at its swizzled position.  Rows past the sequence end fall outside
+  // the descriptor's range and read as zeros.
+  const int64_t seq_elems = (int64_t)s * Hkv * kD;
+  const int nbytes = L * Hkv * kRowBytes;  // the sequence's K (or V) rows
+  const int tile_stride = kBK * Hkv * kRowBytes;
+  const i32x4 rk = buffer_rsrc(p.k + seq_elems, nbytes);
+  const i32x4 rv = buffer_rsrc(p.v + seq_elems, nbytes);
+  int voff[2];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int row = (2 * w + it) * 8 + (lane >> 3);
+    const int data_ch = (lane & 7) ^ swz_key(row);
+    voff[it] = (row * Hkv + g) * kRowBytes + data_ch * 16;
+  }
+  const uint32_t lds_k_base = lds_addr(lds_k) + w * 2048;  // this wave's part of slot 0
+  const uint32_t lds_v_base = lds_addr(lds_v) + w * 2048;
+  auto issue_tile = [&](int t, int buf) {
+    const int off = t * tile_stride;  // carried in the VGPR offset, which the range check covers
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      lds_dma16(lds_k_base + buf * kTileBytes + it * 1024, rk, off + voff[it]);
+      lds_dma16(lds_v_base + buf * kTileBytes + it * 1024, rv, off + voff[it]);
+    }
+  };
+
   const int r16 = lane & 15;
   const int half16 = (lane >> 4) & 1;
-  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 
+  issue_tile(kt0, 0);
   for (int kt = kt0; kt <= kt1; ++kt) {
     const int buf = (kt - kt0) & 1;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads have landed in LDS
-    __syncthreads();                     // every wave's have; tile kt-1 is fully consumed
+    wait_vmem<0>();   // this wave's loads of tile kt have landed
+    __syncthreads();  // every wave's have; tile kt - 1 is fully consumed
     if (kt < kt1) issue_tile(kt + 1, buf ^ 1);
-    const u32x4* kt_lds = &lds_k[buf * kTileChunks];
-    lds_char* vbase = (lds_char*)&lds_v[buf * kTileChunks];
+    const u32x4* kl = &lds_k[buf * kTileChunks];
+    lds_char* vb = (lds_char*)&lds_v[buf * kTileChunks];
 
     // ---- S^T = K Q^T for 64 keys x this wave's 64 queries
     f32x16 sacc[2][2];
@@ -232,28 +288,32 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const int key = 32 * mb + l32;
-        const bf16x8 a = __builtin_bit_cast(bf16x8, kt_lds[swz(key, 2 * ks + hi)]);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, kl[swz(key, 2 * ks + hi)]);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
           sacc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[nb][ks], sacc[mb][nb], 0, 0, 0);
       }
     }
 
-    // ---- mask (only tiles not fully visible to every row of the work-group)
+    // ---- mask (only tiles not fully visible to every row of the work-group);
+    // element (mb, e) holds key k0 + 4 hi + c with c = 32 mb + 8 (e / 4) + e % 4,
+    // compared against this lane's diagonal offset so that c stays an immediate
     const int k0 = kt * kBK;
     const bool need_mask = (k0 + kBK - 1 > p0) || (WINDOWED && (p0 + P - 1) - k0 >= p.window);
     if (need_mask) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int nb = 0; nb < 2; ++nb) {
+        const int di = pos[nb] - k0 - 4 * hi;
+        const int dw = di - p.window;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const int j = k0 + 32 * mb + 8 * (e / 4) + 4 * hi + (e % 4);
-            const int i = pos[nb];
-            const bool vis = (j <= i) && (!WINDOWED || i - j < p.window);
-            if (!vis) sacc[mb][nb][e] = -INFINITY;
+            const int c = 32 * mb + 8 * (e / 4) + (e % 4);
+            const bool vis = (c <= di) && (!WINDOWED || c > dw);
+            sacc[mb][nb][e] = vis ? sacc[mb][nb][e] : -INFINITY;
           }
+      }
     }
 
     // ---- raise the reference maxima only when a row outgrows them by > 2^8
@@ -280,19 +340,18 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const float muse = (mref[nb] == -INFINITY) ? 0.f : mref[nb];
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
+        for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            pf[2 * mb + h2][nb][e] =
-                (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[mb][nb][8 * h2 + e], p.c, -muse));
-          const bf16x8 v8 = pf[2 * mb + h2][nb];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            lsum[nb] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v8[2 * e], v8[2 * e + 1]}, ones, lsum[nb], false);
-        }
+          for (int e = 0; e < 8; ++e) {
+            const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[mb][nb][8 * h2 + e], p.c, -muse));
+            pf[2 * mb + h2][nb][e] = (__bf16)pe;
+            part[e & 3] += pe;
+          }
+      lsum[nb] += (part[0] + part[1]) + (part[2] + part[3]);
     }
 
     // ---- O^T += V^T P^T; lane l of step s4 needs keys 16 s4 + 8 (e / 4) + 4 hi + e % 4
@@ -303,10 +362,10 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
         const int d = 32 * db + 16 * half16 + 4 * (r16 & 3);
-        const int off_lo = key_lo * kRowBytes + (((d >> 3) ^ (key_lo & 7)) << 4) + (d & 7) * 2;
-        const int off_hi = key_hi * kRowBytes + (((d >> 3) ^ (key_hi & 7)) << 4) + (d & 7) * 2;
-        const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + off_lo));
-        const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + off_hi));
+        const int off_lo = key_lo * kRowBytes + (((d >> 3) ^ swz_key(key_lo)) << 4) + (d & 7) * 2;
+        const int off_hi = key_hi * kRowBytes + (((d >> 3) ^ swz_key(key_hi)) << 4) + (d & 7) * 2;
+        const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + off_lo));
+        const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + off_hi));
         const u32x2 u0 = __builtin_bit_cast(u32x2, t0);
         const u32x2 u1 = __builtin_bit_cast(u32x2, t1);
         const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{u0[0], u0[1], u1[0], u1[1]});
