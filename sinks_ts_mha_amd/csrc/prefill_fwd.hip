@@ -38,20 +38,33 @@
 // lands in the XOR-swizzled layout the readers expect.  The XOR pattern is laid
 // out for an LDS that serves 256 bytes (64 banks) per cycle.
 //
-// Softmax.  Online (streaming) softmax in base 2: t = s * scale * log2(e).  The
-// reference maximum of each row starts at the sink's logit (times log2 e), so
-// the sink takes part in the maximum, and the sink's own term exp2(sigma - m)
-// is added to the denominator once, at the end.  The reference is raised only
-// when a tile's row maximum exceeds it by more than 8 (a factor 256), so the
-// rescaling of the accumulators is rare; probabilities stay below 2^8 and fp32
-// sums cannot overflow.  Row sums are plain fp32 adds of the probabilities in
-// four independent chains (the packed bf16 dot instruction would halve their
-// count, but on gfx950 it shares the matrix pipeline and waits behind MFMAs of
-// the other wave on the SIMD).  A row with no visible key so far uses 0 as its
-// reference, so no inf - inf occurs.
+// Softmax.  Base 2 throughout: t = s * scale * log2(e).  A row's result does
+// not depend on the reference m its probabilities exp2(t - m) are measured
+// against, as long as nothing leaves fp32 range, so the fast pass fixes m per
+// row up front: the larger of the sink's logit and the logit of the row's own
+// key (a dot product taken in the prologue).  The row's running maximum
+// reaches that value, so probabilities are never smaller than under a
+// streaming softmax and no rescaling is needed; there is no per-element
+// maximum at all.  Row sums accumulate on the matrix pipe (see row_sums), so
+// the per-element vector work is one fma, one exp2 and half a bf16 pack.  If a
+// row's logits climb so far above its reference that a sum passes 2^64 or a
+// value stops being finite, the work-group redoes its rows with a streaming
+// softmax with running maxima (tile_exact); that pass sums in fp32 on the
+// vector units.  The sink's own term exp2(sigma - m) joins the denominator at
+// the end.
+//
+// Scheduling.  Each tile runs in six steps over its four 32 x 32 score
+// blocks; the softmax of one block is interleaved instruction by instruction
+// with the MFMAs of its neighbours (sched_group_barrier), so a wave keeps the
+// matrix pipe and the vector ALU busy at the same time.  Tiles that need the
+// causal or window mask start their score accumulators from a 0 / -inf mask,
+// and run in loops of their own, so that each loop body holds a single kind of
+// tile.
 #include "prefill_fwd.h"
 
 #include <math.h>
+
+#include <type_traits>
 
 namespace tsmha {
 
@@ -60,6 +73,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -77,7 +91,7 @@ constexpr int kChunks = kRowBytes / 16;       // 16-byte chunks per row
 constexpr int kTileChunks = kBK * kChunks;    // 16-byte chunks per tile
 constexpr int kTileBytes = kTileChunks * 16;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescaleSlack = 8.f;          // log2 units the reference max may lag by
+constexpr float kFastSumLimit = 1.8446744e19f;  // 2^64: largest row sum the fast pass keeps
 constexpr int kBufferConfig = 0x00020000;     // raw buffer descriptor word 3 (32-bit data)
 constexpr int kSlots = 2;                     // LDS buffers for K and for V tiles
 
@@ -118,16 +132,15 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-// Maximum of 32 values: two independent chains of 3-input maxima (v_max3_f32).
-__device__ __forceinline__ float max32(const f32x16& a, const f32x16& b) {
+// Maximum of the 16 values of one accumulator block: two chains of 3-input maxima.
+__device__ __forceinline__ float max16(const f32x16& a) {
   float x = fmaxf(fmaxf(a[0], a[1]), a[2]);
-  float y = fmaxf(fmaxf(b[0], b[1]), b[2]);
-#pragma unroll
-  for (int i = 3; i < 15; i += 2) {
-    x = fmaxf(fmaxf(x, a[i]), a[i + 1]);
-    y = fmaxf(fmaxf(y, b[i]), b[i + 1]);
-  }
-  return fmaxf(fmaxf(x, a[15]), fmaxf(y, b[15]));
+  float y = fmaxf(fmaxf(a[3], a[4]), a[5]);
+  x = fmaxf(fmaxf(x, a[6]), a[7]);
+  y = fmaxf(fmaxf(y, a[8]), a[9]);
+  x = fmaxf(fmaxf(x, a[10]), a[11]);
+  y = fmaxf(fmaxf(y, a[12]), a[13]);
+  return fmaxf(fmaxf(x, a[14]), fmaxf(y, a[15]));
 }
 
 // Raw buffer descriptor (base, stride 0, byte range n) in scalar registers.
@@ -178,6 +191,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   constexpr int P = kRows / G;  // positions per work-group
   __shared__ u32x4 lds_k[kSlots * kTileChunks];
   __shared__ u32x4 lds_v[kSlots * kTileChunks];
+  __shared__ int redo_vote[kWaves];
 
   const int Hkv = p.n_kv_heads;
   const int Hq = Hkv * G;
@@ -200,38 +214,51 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   const int w = tid >> 6;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
+  const int r16 = lane & 15;
+  const int half16 = (lane >> 4) & 1;
+  const float c = p.c;
 
   const int last = min(L, p0 + P) - 1;
   const int first = WINDOWED ? max(0, p0 - p.window + 1) : 0;
   const int kt0 = first / kBK;
   const int kt1 = last / kBK;
 
-  // ---- this lane's two query rows (one per 32-column block nb)
+  // ---- this lane's two query rows (one per 32-column block nb).  Lane l holds
+  // head_dim elements 16 ks + 8 hi .. + 7 of its row for ks = 0..3.
   int pos[2], head[2];
   bf16x8 qf[2][4];
   float mref[2], lsum[2];
   f32x16 o[2][2];  // [d block][nb]: O^T, rows = head_dim, columns = queries
+  float sink_t[2];  // the sink logit times log2 e (-inf without sinks)
+  float diag_t[2];  // the row's own key's logit times log2 e, to about fp32 accuracy
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int r = 64 * w + 32 * nb + l32;
     head[nb] = g * G + r % G;
     pos[nb] = p0 + r / G;
+    sink_t[nb] = p.sinks ? p.sinks[head[nb]] * kLog2e : -INFINITY;
+    float dot = 0.f;
     if (pos[nb] < L) {
       const uint16_t* qrow = p.q + ((int64_t)(s + pos[nb]) * Hq + head[nb]) * kD + 8 * hi;
+      const uint16_t* krow = p.k + ((int64_t)(s + pos[nb]) * Hkv + g) * kD + 8 * hi;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 0; ks < 4; ++ks) {
         qf[nb][ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * ks));
+        const u32x4 kk = *(const u32x4*)(krow + 16 * ks);
+        const u32x4 qq = __builtin_bit_cast(u32x4, qf[nb][ks]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qq[j]),
+                                                __builtin_bit_cast(bf16x2, kk[j]), dot, false);
+      }
     } else {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) qf[nb][ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
     }
-    mref[nb] = p.sinks ? p.sinks[head[nb]] * kLog2e : -INFINITY;
-    lsum[nb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[db][nb][e] = 0.f;
+    diag_t[nb] = pair_sum(dot) * c;
   }
+  // The Q and K loads above must complete here, not inside the tile loop.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // ---- K/V staging, double-buffered: tile t lives in slot (t - kt0) mod 2.
   // The loads of tile t + 1 are issued right after the barrier that opens tile
@@ -263,124 +290,262 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
     }
   };
 
-  const int r16 = lane & 15;
-  const int half16 = (lane >> 4) & 1;
-
-  issue_tile(kt0, 0);
-  for (int kt = kt0; kt <= kt1; ++kt) {
-    const int buf = (kt - kt0) & 1;
-    wait_vmem<0>();   // this wave's loads of tile kt have landed
-    __syncthreads();  // every wave's have; tile kt - 1 is fully consumed
-    if (kt < kt1) issue_tile(kt + 1, buf ^ 1);
-    const u32x4* kl = &lds_k[buf * kTileChunks];
-    lds_char* vb = (lds_char*)&lds_v[buf * kTileChunks];
-
-    // ---- S^T = K Q^T for 64 keys x this wave's 64 queries
-    f32x16 sacc[2][2];
+  // K fragments (A operand) of key half mb for the four 16-wide steps of head_dim.
+  auto read_k = [&](const u32x4* kl, int mb, bf16x8 (&ka)[4]) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int ks = 0; ks < 4; ++ks)
+      ka[ks] = __builtin_bit_cast(bf16x8, kl[swz(32 * mb + l32, 2 * ks + hi)]);
+  };
+  // V^T fragments (A operand of the PV MFMA) of PV step s4 (keys 16 s4 .. +15), both d blocks.
+  auto read_v = [&](lds_char* vb, int s4, bf16x8 (&va)[2]) {
+    const int key_lo = 16 * s4 + 4 * hi + (r16 >> 2);
+    const int key_hi = key_lo + 8;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+    for (int db = 0; db < 2; ++db) {
+      const int d = 32 * db + 16 * half16 + 4 * (r16 & 3);
+      const int off_lo = key_lo * kRowBytes + (((d >> 3) ^ swz_key(key_lo)) << 4) + (d & 7) * 2;
+      const int off_hi = key_hi * kRowBytes + (((d >> 3) ^ swz_key(key_hi)) << 4) + (d & 7) * 2;
+      const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + off_lo));
+      const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + off_hi));
+      const u32x2 u0 = __builtin_bit_cast(u32x2, t0);
+      const u32x2 u1 = __builtin_bit_cast(u32x2, t1);
+      va[db] = __builtin_bit_cast(bf16x8, u32x4{u0[0], u0[1], u1[0], u1[1]});
+    }
+  };
+  // Scores of the 32 x 32 block (key half mb, query block nb).  On tiles that
+  // are not fully visible the accumulator starts from the mask (0 for a
+  // visible key, -inf for a hidden one), so the MFMA applies it.  Element e
+  // holds key k0 + 4 hi + 32 mb + 8 (e / 4) + e % 4, compared against the
+  // lane's diagonal offset so that the key offset stays an immediate.
+  auto qk = [&](auto masked_tag, const bf16x8 (&ka)[4], int mb, int nb, int k0) -> f32x16 {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    f32x16 acc = {};
+    if constexpr (MASKED) {
+      const int di = pos[nb] - k0 - 4 * hi;
+      const int dw = di - p.window;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[mb][nb][e] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int key = 32 * mb + l32;
-        const bf16x8 a = __builtin_bit_cast(bf16x8, kl[swz(key, 2 * ks + hi)]);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          sacc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[nb][ks], sacc[mb][nb], 0, 0, 0);
+      for (int e = 0; e < 16; ++e) {
+        const int cc = 32 * mb + 8 * (e / 4) + (e % 4);
+        const bool vis = (cc <= di) && (!WINDOWED || cc > dw);
+        acc[e] = vis ? 0.f : -INFINITY;
       }
     }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[nb][ks], acc, 0, 0, 0);
+    return acc;
+  };
+  // Probabilities of one score block against reference m, as bf16 P^T in the
+  // PV B-operand order (plo: PV step 2 mb, phi: step 2 mb + 1).  Hidden keys
+  // arrive as -inf and give 0.  The exact pass also returns the lane's sum of
+  // the fp32 values.
+  auto block_probs = [&](const f32x16& sc, float m, bf16x8& plo, bf16x8& phi) -> float {
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float pe = __builtin_amdgcn_exp2f(fmaf(sc[e], c, -m));
+      if (e < 8) plo[e] = (__bf16)pe; else phi[e - 8] = (__bf16)pe;
+      if (e & 1) a1 += pe; else a0 += pe;
+    }
+    return a0 + a1;
+  };
+  auto block_probs_nosum = [&](const f32x16& sc, float m, bf16x8& plo, bf16x8& phi) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float pe = __builtin_amdgcn_exp2f(fmaf(sc[e], c, -m));
+      if (e < 8) plo[e] = (__bf16)pe; else phi[e - 8] = (__bf16)pe;
+    }
+  };
+  // Row sums of the fast pass run on the matrix pipe: a 16 x 16 x 32 MFMA
+  // whose A operand is a fixed 0/1 selector reads a P^T fragment as its
+  // B operand.  Of the 64 lanes holding one 16-key step of 32 queries, lanes
+  // n and n + 32 carry query n and lanes n + 16, n + 48 query n + 16; row 0
+  // of the selector picks the first pair and row 1 the second, so output
+  // rows 0 and 1 (lanes 0..15, elements 0 and 1) accumulate the sums of the
+  // bf16 probabilities of queries n and n + 16.
+  const int lsel = ((lane & 15) == 0 && ((lane >> 4) & 1) == 0) || ((lane & 15) == 1 && ((lane >> 4) & 1) == 1);
+  const bf16x8 sel = __builtin_bit_cast(bf16x8, lsel ? u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u}
+                                                     : u32x4{0u, 0u, 0u, 0u});
+  f32x4 lacc[2];
+  auto row_sums = [&](const bf16x8 (&pf)[4][2], int mb, int nb) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      lacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pf[2 * mb + j][nb], lacc[nb], 0, 0, 0);
+  };
+  // O^T += V^T P^T over the 32 keys of half mb (PV steps 2 mb, 2 mb + 1) for query block nb.
+  auto pv = [&](const bf16x8 (&va)[2][2], const bf16x8 (&pf)[4][2], int mb, int nb) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+        o[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j][db], pf[2 * mb + j][nb], o[db][nb], 0, 0, 0);
+  };
+  // One MFMA, then n VALU instructions, k times (the order within a step).
+  auto interleave = [](auto k_tag, auto n_tag) {
+    constexpr int k = decltype(k_tag)::value;
+    constexpr int n = decltype(n_tag)::value;
+#pragma unroll
+    for (int i = 0; i < k; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, n, 0);
+    }
+  };
 
-    // ---- mask (only tiles not fully visible to every row of the work-group);
-    // element (mb, e) holds key k0 + 4 hi + c with c = 32 mb + 8 (e / 4) + e % 4,
-    // compared against this lane's diagonal offset so that c stays an immediate
-    const int k0 = kt * kBK;
-    const bool need_mask = (k0 + kBK - 1 > p0) || (WINDOWED && (p0 + P - 1) - k0 >= p.window);
-    if (need_mask) {
+  // ---- fast tile: every row keeps its reference fixed (no maxima, no
+  // rescaling), and row sums accumulate on the matrix pipe.  The tile runs as
+  // six steps over its four 32 x 32 blocks so that each block's softmax
+  // overlaps the MFMAs of its neighbours:
+  //   0: scores (0,0) (0,1)            1: scores (1,0) | probs (0,0)
+  //   2: scores (1,1) | probs (0,1)    3: PV (0,0)     | probs (1,0)
+  //   4: PV (0,1)     | probs (1,1)    5: PV (1,0) (1,1)
+  using I4 = std::integral_constant<int, 4>;
+  using I6 = std::integral_constant<int, 6>;
+  auto tile_fast = [&](auto masked_tag, const u32x4* kl, lds_char* vb, int k0) {
+    bf16x8 ka[4], kb[4], pf[4][2], va[2][2], vc[2][2];
+    read_k(kl, 0, ka);
+    read_k(kl, 1, kb);
+    const f32x16 s00 = qk(masked_tag, ka, 0, 0, k0);
+    const f32x16 s01 = qk(masked_tag, ka, 0, 1, k0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_v(vb, 0, va[0]);
+    read_v(vb, 1, va[1]);
+    const f32x16 s10 = qk(masked_tag, kb, 1, 0, k0);
+    block_probs_nosum(s00, mref[0], pf[0][0], pf[1][0]);
+    interleave(I4{}, std::integral_constant<int, 10>{});
+    __builtin_amdgcn_sched_barrier(0);
+    const f32x16 s11 = qk(masked_tag, kb, 1, 1, k0);
+    block_probs_nosum(s01, mref[1], pf[0][1], pf[1][1]);
+    interleave(I4{}, std::integral_constant<int, 10>{});
+    __builtin_amdgcn_sched_barrier(0);
+    read_v(vb, 2, vc[0]);
+    read_v(vb, 3, vc[1]);
+    pv(va, pf, 0, 0);
+    row_sums(pf, 0, 0);
+    block_probs_nosum(s10, mref[0], pf[2][0], pf[3][0]);
+    interleave(I6{}, std::integral_constant<int, 7>{});
+    __builtin_amdgcn_sched_barrier(0);
+    pv(va, pf, 0, 1);
+    row_sums(pf, 0, 1);
+    block_probs_nosum(s11, mref[1], pf[2][1], pf[3][1]);
+    interleave(I6{}, std::integral_constant<int, 7>{});
+    __builtin_amdgcn_sched_barrier(0);
+    pv(vc, pf, 1, 0);
+    row_sums(pf, 1, 0);
+    pv(vc, pf, 1, 1);
+    row_sums(pf, 1, 1);
+  };
+
+  // ---- exact tile: streaming softmax with running maxima, used only when the
+  // fast pass of this work-group overflowed.  Each key half raises the row
+  // maxima, rescales the accumulators, then adds its probabilities.
+  auto tile_exact = [&](auto masked_tag, const u32x4* kl, lds_char* vb, int k0) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      bf16x8 ka[4], pf[4][2], va[2][2];
+      read_k(kl, mb, ka);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        const int di = pos[nb] - k0 - 4 * hi;
-        const int dw = di - p.window;
+        const f32x16 sc = qk(masked_tag, ka, mb, nb, k0);
+        const float mx = pair_max(max16(sc)) * c;
+        if (mx > mref[nb]) {
+          const float alpha = __builtin_amdgcn_exp2f(mref[nb] - mx);
+          lsum[nb] *= alpha;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+          for (int db = 0; db < 2; ++db)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int c = 32 * mb + 8 * (e / 4) + (e % 4);
-            const bool vis = (c <= di) && (!WINDOWED || c > dw);
-            sacc[mb][nb][e] = vis ? sacc[mb][nb][e] : -INFINITY;
-          }
+            for (int e = 0; e < 16; ++e) o[db][nb][e] *= alpha;
+          mref[nb] = mx;
+        }
+        const float m = (mref[nb] == -INFINITY) ? 0.f : mref[nb];
+        lsum[nb] += block_probs(sc, m, pf[2 * mb][nb], pf[2 * mb + 1][nb]);
       }
+      read_v(vb, 2 * mb, va[0]);
+      read_v(vb, 2 * mb + 1, va[1]);
+      pv(va, pf, mb, 0);
+      pv(va, pf, mb, 1);
     }
+  };
 
-    // ---- raise the reference maxima only when a row outgrows them by > 2^8
-    float mcand[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) mcand[nb] = pair_max(max32(sacc[0][nb], sacc[1][nb])) * p.c;
-    const bool grow = (mcand[0] > mref[0] + kRescaleSlack) || (mcand[1] > mref[1] + kRescaleSlack);
-    if (__any(grow)) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const float mnew = fmaxf(mref[nb], mcand[nb]);
-        const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mref[nb] - mnew);
-        lsum[nb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[db][nb][e] *= alpha;
-        mref[nb] = mnew;
-      }
+  // Walk the tiles of this work-group's key range.  Only tiles that are not
+  // fully visible to every row of the work-group take the mask: tiles
+  // [kt0, ktA) may hold keys that left some row's window, tiles [ktB, kt1]
+  // keys past some row's position.  The three runs are separate loops so that
+  // each loop body holds one kind of tile.
+  //   unmasked <=> k0 + kBK - 1 <= p0  and (no window or (p0 + P - 1) - k0 < window)
+  const int ktB = max(kt0, min(kt1 + 1, (p0 + 1) / kBK));  // first tile with k0 + kBK - 1 > p0
+  const int xa = p0 + P - p.window;  // first tile with k0 >= xa: all its keys inside every window
+  const int ktA = (WINDOWED && xa > 0) ? min(ktB, max(kt0, (xa + kBK - 1) / kBK)) : kt0;
+  auto walk = [&](auto tile_fn, auto masked_tag, int kt_begin, int kt_end) {
+    for (int kt = kt_begin; kt < kt_end; ++kt) {
+      const int buf = (kt - kt0) & 1;
+      wait_vmem<0>();   // this wave's loads of tile kt have landed
+      __syncthreads();  // every wave's have; tile kt - 1 is fully consumed
+      if (kt < kt1) issue_tile(kt + 1, buf ^ 1);
+      tile_fn(masked_tag, &lds_k[buf * kTileChunks], (lds_char*)&lds_v[buf * kTileChunks], kt * kBK);
     }
-
-    // ---- probabilities, bf16 P^T in the PV B-operand order, row sums of the bf16 values
-    bf16x8 pf[4][2];
+  };
+  auto reset = [&](bool exact) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const float muse = (mref[nb] == -INFINITY) ? 0.f : mref[nb];
-      float part[4] = {0.f, 0.f, 0.f, 0.f};
+      // Fast pass: the reference is max(sink, own key's logit), a value the
+      // row's running maximum reaches, so probabilities are never below their
+      // streaming-softmax values and their sum is at least about 1.
+      mref[nb] = exact ? sink_t[nb] : fmaxf(sink_t[nb], diag_t[nb]);
+      lsum[nb] = 0.f;
+      lacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int db = 0; db < 2; ++db)
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[mb][nb][8 * h2 + e], p.c, -muse));
-            pf[2 * mb + h2][nb][e] = (__bf16)pe;
-            part[e & 3] += pe;
-          }
-      lsum[nb] += (part[0] + part[1]) + (part[2] + part[3]);
+        for (int e = 0; e < 16; ++e) o[db][nb][e] = 0.f;
     }
+  };
 
-    // ---- O^T += V^T P^T; lane l of step s4 needs keys 16 s4 + 8 (e / 4) + 4 hi + e % 4
+  reset(false);
+  issue_tile(kt0, 0);
+  walk(tile_fast, std::true_type{}, kt0, ktA);
+  walk(tile_fast, std::false_type{}, ktA, ktB);
+  walk(tile_fast, std::true_type{}, ktB, kt1 + 1);
+  // Each lane takes its row's sum from the row-sum accumulators: query q of
+  // block nb sits in lane q % 16, element q / 16.
+  float lrow[2];
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const int key_lo = 16 * s4 + 4 * hi + (r16 >> 2);
-      const int key_hi = key_lo + 8;
+  for (int nb = 0; nb < 2; ++nb) {
+    const float e0 = __shfl(lacc[nb][0], l32 & 15);
+    const float e1 = __shfl(lacc[nb][1], l32 & 15);
+    lrow[nb] = (l32 < 16) ? e0 : e1;
+  }
+  // The fast pass is kept unless some row's probabilities grew so far past its
+  // reference that the sums lost range: a row sum above 2^64, or a sum or an
+  // output that is not finite.  Then the work-group redoes its rows exactly.
+  {
+    bool bad = false;
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        const int d = 32 * db + 16 * half16 + 4 * (r16 & 3);
-        const int off_lo = key_lo * kRowBytes + (((d >> 3) ^ swz_key(key_lo)) << 4) + (d & 7) * 2;
-        const int off_hi = key_hi * kRowBytes + (((d >> 3) ^ swz_key(key_hi)) << 4) + (d & 7) * 2;
-        const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + off_lo));
-        const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + off_hi));
-        const u32x2 u0 = __builtin_bit_cast(u32x2, t0);
-        const u32x2 u1 = __builtin_bit_cast(u32x2, t1);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{u0[0], u0[1], u1[0], u1[1]});
+    for (int nb = 0; nb < 2; ++nb) {
+      float osum = 0.f;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          o[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[s4][nb], o[db][nb], 0, 0, 0);
-      }
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) osum += o[db][nb][e];
+      bad = bad || !(lrow[nb] <= kFastSumLimit) || !(fabsf(osum) <= 3.0e38f);
+    }
+    const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+    if (lane == 0) redo_vote[w] = wave_bad ? 1 : 0;
+    __syncthreads();
+    const bool redo = (redo_vote[0] | redo_vote[1] | redo_vote[2] | redo_vote[3]) != 0;
+    if (redo) {
+      reset(true);
+      issue_tile(kt0, 0);
+      walk(tile_exact, std::true_type{}, kt0, kt1 + 1);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) lrow[nb] = pair_sum(lsum[nb]);
     }
   }
 
-  // ---- epilogue: combine the two half-sums, add the sink's term, normalise, store
+  // ---- epilogue: add the sink's term to the row sum, normalise, store
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    float lt = pair_sum(lsum[nb]);
-    if (p.sinks) lt += __builtin_amdgcn_exp2f(p.sinks[head[nb]] * kLog2e - mref[nb]);
+    float lt = lrow[nb];
+    if (p.sinks) lt += __builtin_amdgcn_exp2f(sink_t[nb] - mref[nb]);
     const float inv = 1.f / lt;
     if (pos[nb] < L) {
       uint16_t* orow = p.out + ((int64_t)(s + pos[nb]) * Hq + head[nb]) * kD;

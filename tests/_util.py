@@ -53,13 +53,15 @@ def rounding_bound(inp: dict, ref, lib=None):
     """Elementwise error allowance of a bf16-P, fp32-accumulate, bf16-output kernel.
 
     bf16 keeps 8 significant bits, so round-to-nearest has unit roundoff
-    u = 2^-8.  Rounding each normalised probability to bf16 moves output
-    element d by at most u * sum_j p_j |v_jd| (sink included in the
-    normalisation), and rounding the output adds u |out_d|.  sum_j p_j |v_jd|
-    is the oracle's output for |v| (bf16 |v| is exact).  fp32 accumulation and
-    the online rescaling add relative terms near 2^-20, covered by a factor
-    (1 + 2^-6) and an absolute 1e-6.
+    u = 2^-8.  Rounding each probability to bf16 moves the weighted sum of
+    output element d by at most u * sum_j p_j |v_jd| (p normalised, sink
+    included).  The kernel's denominator is the sum of those same rounded
+    probabilities plus the sink's term, which moves the normalisation by at
+    most u relative, i.e. the output by u |out_d|; rounding the output to bf16
+    adds another u |out_d|.  sum_j p_j |v_jd| is the oracle's output for |v|
+    (bf16 |v| is exact).  fp32 accumulation adds relative terms near 2^-20,
+    covered by a factor (1 + 2^-6) and an absolute 1e-6.
     """
     from oracle import oracle
     weighted_abs = oracle.prefill(*oracle_args(dict(inp, v=inp["v"].abs())), lib=lib)
-    return 2.0 ** -8 * (1 + 2.0 ** -6) * (weighted_abs + np.abs(ref)) + 1e-6
+    return 2.0 ** -8 * (1 + 2.0 ** -6) * (weighted_abs + 2.0 * np.abs(ref)) + 1e-6

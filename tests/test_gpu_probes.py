@@ -54,12 +54,13 @@ Q_ZERO_CASES = [("gptoss_full_4x2048", 0), ("gptoss_window128_4x2048", 128),
 @pytest.mark.parametrize("name,window", Q_ZERO_CASES)
 @pytest.mark.parametrize("sink_range", [(0.0, 3.0), (-3.0, 3.0)], ids=["sinks_nonneg", "sinks_mixed"])
 def test_q_zero_closed_form(name, window, sink_range):
-    """With sinks >= 0 every probability of a row is exp(-sigma) <= 1 against the
-    sink-initialised reference, the reference never moves, and all probabilities
-    round alike: |err| <= 2^-7 |ref|.  With negative sinks the kernel may raise
-    its reference part-way through a row, so probabilities from different tiles
-    round independently; the general bound u (sum_j p_j |v_j| + |out|) applies,
-    with sum_j p_j |v_j| given by the same closed form on |v|."""
+    """With q = 0 every logit of a row is 0, so every probability of the row is
+    one number: exp(-sigma) against a sink reference, or 1.  All of them round
+    alike, the rounded denominator carries the same relative error, and the
+    output rounding adds u: |err| <= 2^-7 |ref|.  The negative-sink cases also
+    get the general bound u (sum_j p_j |v_j| + 2 |out|), with sum_j p_j |v_j|
+    given by the same closed form on |v|, should the reference differ between
+    tiles."""
     wl = workloads.WORKLOADS[name]
     inp = workloads.make_inputs(wl)
     inp["q"] = torch.zeros_like(inp["q"])
@@ -73,7 +74,7 @@ def test_q_zero_closed_form(name, window, sink_range):
         bound = 2.0 ** -7 * (1 + 2.0 ** -6) * np.abs(ref) + 1e-5
     else:
         weighted_abs = q_zero_reference(dict(inp, v=inp["v"].abs()))
-        bound = 2.0 ** -8 * (1 + 2.0 ** -6) * (weighted_abs + np.abs(ref)) + 1e-6
+        bound = 2.0 ** -8 * (1 + 2.0 ** -6) * (weighted_abs + 2.0 * np.abs(ref)) + 1e-6
     if not np.all(err <= bound):
         excess = (err - bound).reshape(-1)
         cu = inp["cu_seqlens"].tolist()
@@ -108,6 +109,25 @@ def test_sink_values(sink, oracle_lib):
     assert np.all(np.abs(got - ref) <= rounding_bound(inp, ref, oracle_lib))
     if sink == 80.0:
         assert np.max(np.abs(got)) < 1e-6
+
+
+@pytest.mark.parametrize("window", [0, 100])
+@pytest.mark.parametrize("with_sinks", [True, False], ids=["sinks", "nosinks"])
+def test_wide_logit_range(window, with_sinks, oracle_lib):
+    """Queries scaled by 40 spread each row's logits over hundreds of log2 units,
+    so measured against the row's own key many probabilities overflow fp32 (or
+    their sums pass 2^64) in the fast pass.  Those work-groups must redo their
+    rows with running maxima; every row still meets the rounding bound."""
+    wl = workloads.custom([700, 333, 64, 5], 16, 2, window=window, seed=6)
+    inp = workloads.make_inputs(wl)
+    inp["q"] = (inp["q"].to(torch.float32) * 40.0).to(torch.bfloat16)
+    if not with_sinks:
+        inp["sinks"] = None
+    say(f"wide logit range window={window} sinks={with_sinks}")
+    got = f64(run_gpu(inp).cpu())
+    ref = oracle.prefill(*oracle_args(inp), lib=oracle_lib)
+    assert np.all(np.isfinite(got))
+    assert np.all(np.abs(got - ref) <= rounding_bound(inp, ref, oracle_lib))
 
 
 def test_edge_shapes(oracle_lib):
