@@ -223,6 +223,40 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   const int kt0 = first / kBK;
   const int kt1 = last / kBK;
 
+  // ---- K/V staging, double-buffered: tile t lives in slot (t - kt0) mod 2.
+  // The loads of tile t + 1 are issued right after the barrier that opens tile
+  // t and land while tile t is consumed.  Wave w fills LDS chunks
+  // [128 w, 128 w + 128) of a tile with two wave-wide loads; the lane-to-LDS
+  // order is fixed by the hardware, so each lane fetches the data chunk that
+  // belongs at its swizzled position.  Rows past the sequence end fall outside
+  // the descriptor's range and read as zeros.
+  const int64_t seq_elems = (int64_t)s * Hkv * kD;
+  const int nbytes = L * Hkv * kRowBytes;  // the sequence's K (or V) rows
+  const int tile_stride = kBK * Hkv * kRowBytes;
+  const i32x4 rk = buffer_rsrc(p.k + seq_elems, nbytes);
+  const i32x4 rv = buffer_rsrc(p.v + seq_elems, nbytes);
+  int voff[2];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int row = (2 * w + it) * 8 + (lane >> 3);
+    const int data_ch = (lane & 7) ^ swz_key(row);
+    voff[it] = (row * Hkv + g) * kRowBytes + data_ch * 16;
+  }
+  const uint32_t lds_k_base = lds_addr(lds_k) + w * 2048;  // this wave's part of slot 0
+  const uint32_t lds_v_base = lds_addr(lds_v) + w * 2048;
+  auto issue_tile = [&](int t, int buf) {
+    const int off = t * tile_stride;  // carried in the VGPR offset, which the range check covers
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      lds_dma16(lds_k_base + buf * kTileBytes + it * 1024, rk, off + voff[it]);
+      lds_dma16(lds_v_base + buf * kTileBytes + it * 1024, rv, off + voff[it]);
+    }
+  };
+  // The first tile's loads go out before the query loads below, so the two
+  // latencies overlap.
+  issue_tile(kt0, 0);
+
+
   // ---- this lane's two query rows (one per 32-column block nb).  Lane l holds
   // head_dim elements 16 ks + 8 hi .. + 7 of its row for ks = 0..3.
   int pos[2], head[2];
@@ -257,56 +291,37 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
     }
     diag_t[nb] = pair_sum(dot) * c;
   }
-  // The Q and K loads above must complete here, not inside the tile loop.
+  // The Q and K loads above (and the first tile's) complete here, not inside
+  // the tile loop.
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
-  // ---- K/V staging, double-buffered: tile t lives in slot (t - kt0) mod 2.
-  // The loads of tile t + 1 are issued right after the barrier that opens tile
-  // t and land while tile t is consumed.  Wave w fills LDS chunks
-  // [128 w, 128 w + 128) of a tile with two wave-wide loads; the lane-to-LDS
-  // order is fixed by the hardware, so each lane fetches the data chunk that
-  // belongs at its swizzled position.  Rows past the sequence end fall outside
-  // the descriptor's range and read as zeros.
-  const int64_t seq_elems = (int64_t)s * Hkv * kD;
-  const int nbytes = L * Hkv * kRowBytes;  // the sequence's K (or V) rows
-  const int tile_stride = kBK * Hkv * kRowBytes;
-  const i32x4 rk = buffer_rsrc(p.k + seq_elems, nbytes);
-  const i32x4 rv = buffer_rsrc(p.v + seq_elems, nbytes);
-  int voff[2];
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int row = (2 * w + it) * 8 + (lane >> 3);
-    const int data_ch = (lane & 7) ^ swz_key(row);
-    voff[it] = (row * Hkv + g) * kRowBytes + data_ch * 16;
-  }
-  const uint32_t lds_k_base = lds_addr(lds_k) + w * 2048;  // this wave's part of slot 0
-  const uint32_t lds_v_base = lds_addr(lds_v) + w * 2048;
-  auto issue_tile = [&](int t, int buf) {
-    const int off = t * tile_stride;  // carried in the VGPR offset, which the range check covers
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      lds_dma16(lds_k_base + buf * kTileBytes + it * 1024, rk, off + voff[it]);
-      lds_dma16(lds_v_base + buf * kTileBytes + it * 1024, rv, off + voff[it]);
-    }
-  };
-
   // K fragments (A operand) of key half mb for the four 16-wide steps of head_dim.
+  // Per-lane byte offsets of the operand reads within a tile, fixed for the
+  // whole walk: rows 32 mb + l32 share their swizzle key with row l32, and the
+  // V rows of PV step s4 share theirs with step 0, so the key half, the PV
+  // step and the LDS slot only add immediate offsets.
+  uint32_t koff[4], vlo_off[2], vhi_off[2];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) koff[ks] = (uint32_t)(swz(l32, 2 * ks + hi) * 16) & 0xffffu;
+#pragma unroll
+  for (int db = 0; db < 2; ++db) {
+    const int key_lo = 4 * hi + (r16 >> 2);
+    const int key_hi = key_lo + 8;
+    const int d = 32 * db + 16 * half16 + 4 * (r16 & 3);
+    vlo_off[db] = (uint32_t)(key_lo * kRowBytes + (((d >> 3) ^ swz_key(key_lo)) << 4) + (d & 7) * 2) & 0xffffu;
+    vhi_off[db] = (uint32_t)(key_hi * kRowBytes + (((d >> 3) ^ swz_key(key_hi)) << 4) + (d & 7) * 2) & 0xffffu;
+  }
   auto read_k = [&](const u32x4* kl, int mb, bf16x8 (&ka)[4]) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      ka[ks] = __builtin_bit_cast(bf16x8, kl[swz(32 * mb + l32, 2 * ks + hi)]);
+      ka[ks] = *(const bf16x8*)((const lds_char*)kl + mb * 32 * kRowBytes + koff[ks]);
   };
   // V^T fragments (A operand of the PV MFMA) of PV step s4 (keys 16 s4 .. +15), both d blocks.
   auto read_v = [&](lds_char* vb, int s4, bf16x8 (&va)[2]) {
-    const int key_lo = 16 * s4 + 4 * hi + (r16 >> 2);
-    const int key_hi = key_lo + 8;
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
-      const int d = 32 * db + 16 * half16 + 4 * (r16 & 3);
-      const int off_lo = key_lo * kRowBytes + (((d >> 3) ^ swz_key(key_lo)) << 4) + (d & 7) * 2;
-      const int off_hi = key_hi * kRowBytes + (((d >> 3) ^ swz_key(key_hi)) << 4) + (d & 7) * 2;
-      const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + off_lo));
-      const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + off_hi));
+      const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + s4 * 16 * kRowBytes + vlo_off[db]));
+      const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + s4 * 16 * kRowBytes + vhi_off[db]));
       const u32x2 u0 = __builtin_bit_cast(u32x2, t0);
       const u32x2 u1 = __builtin_bit_cast(u32x2, t1);
       va[db] = __builtin_bit_cast(bf16x8, u32x4{u0[0], u0[1], u1[0], u1[1]});
@@ -501,7 +516,6 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   };
 
   reset(false);
-  issue_tile(kt0, 0);
   walk(tile_fast, std::true_type{}, kt0, ktA);
   walk(tile_fast, std::false_type{}, ktA, ktB);
   walk(tile_fast, std::true_type{}, ktB, kt1 + 1);
