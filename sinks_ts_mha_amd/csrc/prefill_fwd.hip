@@ -40,18 +40,19 @@
 //
 // Softmax.  Base 2 throughout: t = s * scale * log2(e).  A row's result does
 // not depend on the reference m its probabilities exp2(t - m) are measured
-// against, as long as nothing leaves fp32 range, so the fast pass fixes m per
-// row up front: the larger of the sink's logit and the logit of the row's own
-// key (a dot product taken in the prologue).  The row's running maximum
-// reaches that value, so probabilities are never smaller than under a
-// streaming softmax and no rescaling is needed; there is no per-element
-// maximum at all.  Row sums accumulate on the matrix pipe (see row_sums), so
-// the per-element vector work is one fma, one exp2 and half a bf16 pack.  If a
-// row's logits climb so far above its reference that a sum passes 2^64 or a
-// value stops being finite, the work-group redoes its rows with a streaming
-// softmax with running maxima (tile_exact); that pass sums in fp32 on the
-// vector units.  The sink's own term exp2(sigma - m) joins the denominator at
-// the end.
+// against, as long as nothing leaves fp32 range.  The tiles are walked from
+// the last to the first: the diagonal tiles (those holding the work-group's
+// own positions) come first and run a streaming softmax with running maxima
+// and fp32 row sums (tile_exact), which leaves every row a reference that is
+// a maximum of its real logits (and of the sink).  The remaining tiles keep
+// that reference fixed: the row's running maximum is at least as large, so
+// probabilities are never smaller than under a streaming softmax and no
+// rescaling is needed; there is no per-element maximum.  Their row sums
+// accumulate on the matrix pipe (see row_sums), so the per-element vector
+// work is one fma, one exp2 and half a bf16 pack.  If a row's logits climb so
+// far above its reference that a sum passes 2^64 or a value stops being
+// finite, the work-group redoes its rows with tile_exact throughout.  The
+// sink's own term exp2(sigma - m) joins the denominator at the end.
 //
 // Scheduling.  Each tile runs in six steps over its four 32 x 32 score
 // blocks; the softmax of one block is interleaved instruction by instruction
@@ -252,9 +253,10 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
       lds_dma16(lds_v_base + buf * kTileBytes + it * 1024, rv, off + voff[it]);
     }
   };
-  // The first tile's loads go out before the query loads below, so the two
+  // Tiles are walked from the last (the diagonal) back to the first.  The
+  // first tile's loads go out before the query loads below, so the two
   // latencies overlap.
-  issue_tile(kt0, 0);
+  issue_tile(kt1, 0);
 
 
   // ---- this lane's two query rows (one per 32-column block nb).  Lane l holds
@@ -264,35 +266,24 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   float mref[2], lsum[2];
   f32x16 o[2][2];  // [d block][nb]: O^T, rows = head_dim, columns = queries
   float sink_t[2];  // the sink logit times log2 e (-inf without sinks)
-  float diag_t[2];  // the row's own key's logit times log2 e, to about fp32 accuracy
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int r = 64 * w + 32 * nb + l32;
     head[nb] = g * G + r % G;
     pos[nb] = p0 + r / G;
     sink_t[nb] = p.sinks ? p.sinks[head[nb]] * kLog2e : -INFINITY;
-    float dot = 0.f;
     if (pos[nb] < L) {
       const uint16_t* qrow = p.q + ((int64_t)(s + pos[nb]) * Hq + head[nb]) * kD + 8 * hi;
-      const uint16_t* krow = p.k + ((int64_t)(s + pos[nb]) * Hkv + g) * kD + 8 * hi;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < 4; ++ks)
         qf[nb][ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * ks));
-        const u32x4 kk = *(const u32x4*)(krow + 16 * ks);
-        const u32x4 qq = __builtin_bit_cast(u32x4, qf[nb][ks]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qq[j]),
-                                                __builtin_bit_cast(bf16x2, kk[j]), dot, false);
-      }
     } else {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) qf[nb][ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
     }
-    diag_t[nb] = pair_sum(dot) * c;
   }
-  // The Q and K loads above (and the first tile's) complete here, not inside
-  // the tile loop.
+  // The Q loads above (and the first tile's) complete here, not inside the
+  // tile loop.
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // K fragments (A operand) of key half mb for the four 16-wide steps of head_dim.
@@ -450,9 +441,12 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
     row_sums(pf, 1, 1);
   };
 
-  // ---- exact tile: streaming softmax with running maxima, used only when the
-  // fast pass of this work-group overflowed.  Each key half raises the row
-  // maxima, rescales the accumulators, then adds its probabilities.
+  // ---- exact tile: streaming softmax with running maxima and fp32 row sums
+  // on the vector ALU.  It runs the diagonal tiles, which come first in the
+  // walk, and so sets each row's reference to a maximum of real logits; and
+  // it runs every tile when the fast pass of a work-group overflowed.  Each
+  // key half raises the row maxima, rescales the accumulators, then adds its
+  // probabilities.
   auto tile_exact = [&](auto masked_tag, const u32x4* kl, lds_char* vb, int k0) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -481,31 +475,32 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
     }
   };
 
-  // Walk the tiles of this work-group's key range.  Only tiles that are not
-  // fully visible to every row of the work-group take the mask: tiles
-  // [kt0, ktA) may hold keys that left some row's window, tiles [ktB, kt1]
-  // keys past some row's position.  The three runs are separate loops so that
-  // each loop body holds one kind of tile.
+  // Walk the tiles of this work-group's key range from the last to the first.
+  // Only tiles that are not fully visible to every row take the mask: tiles
+  // [ktB, kt1] hold keys past some row's position (they also hold every row's
+  // own key), tiles [kt0, ktA) may hold keys that left some row's window.
   //   unmasked <=> k0 + kBK - 1 <= p0  and (no window or (p0 + P - 1) - k0 < window)
+  // The diagonal tiles run exactly (running maxima); after them each row's
+  // reference stays fixed, a maximum the row's running maximum reaches, so
+  // the remaining probabilities are never below their streaming-softmax
+  // values.  The runs are separate loops so that each loop body holds one
+  // kind of tile.
   const int ktB = max(kt0, min(kt1 + 1, (p0 + 1) / kBK));  // first tile with k0 + kBK - 1 > p0
   const int xa = p0 + P - p.window;  // first tile with k0 >= xa: all its keys inside every window
   const int ktA = (WINDOWED && xa > 0) ? min(ktB, max(kt0, (xa + kBK - 1) / kBK)) : kt0;
-  auto walk = [&](auto tile_fn, auto masked_tag, int kt_begin, int kt_end) {
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
-      const int buf = (kt - kt0) & 1;
+  auto walk = [&](auto tile_fn, auto masked_tag, int kt_hi, int kt_lo) {
+    for (int kt = kt_hi; kt >= kt_lo; --kt) {
+      const int buf = (kt1 - kt) & 1;
       wait_vmem<0>();   // this wave's loads of tile kt have landed
-      __syncthreads();  // every wave's have; tile kt - 1 is fully consumed
-      if (kt < kt1) issue_tile(kt + 1, buf ^ 1);
+      __syncthreads();  // every wave's have; the previous tile is fully consumed
+      if (kt > kt0) issue_tile(kt - 1, buf ^ 1);
       tile_fn(masked_tag, &lds_k[buf * kTileChunks], (lds_char*)&lds_v[buf * kTileChunks], kt * kBK);
     }
   };
-  auto reset = [&](bool exact) {
+  auto reset = [&]() {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      // Fast pass: the reference is max(sink, own key's logit), a value the
-      // row's running maximum reaches, so probabilities are never below their
-      // streaming-softmax values and their sum is at least about 1.
-      mref[nb] = exact ? sink_t[nb] : fmaxf(sink_t[nb], diag_t[nb]);
+      mref[nb] = sink_t[nb];
       lsum[nb] = 0.f;
       lacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -515,18 +510,19 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
     }
   };
 
-  reset(false);
-  walk(tile_fast, std::true_type{}, kt0, ktA);
-  walk(tile_fast, std::false_type{}, ktA, ktB);
-  walk(tile_fast, std::true_type{}, ktB, kt1 + 1);
-  // Each lane takes its row's sum from the row-sum accumulators: query q of
-  // block nb sits in lane q % 16, element q / 16.
+  reset();
+  walk(tile_exact, std::true_type{}, kt1, ktB);
+  walk(tile_fast, std::false_type{}, ktB - 1, ktA);
+  if constexpr (WINDOWED) walk(tile_fast, std::true_type{}, ktA - 1, kt0);
+  // A row's sum: its diagonal tiles' fp32 sums (split over the lane pair) plus
+  // the row-sum accumulators of the other tiles, where query q of block nb
+  // sits in lane q % 16, element q / 16.
   float lrow[2];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const float e0 = __shfl(lacc[nb][0], l32 & 15);
     const float e1 = __shfl(lacc[nb][1], l32 & 15);
-    lrow[nb] = (l32 < 16) ? e0 : e1;
+    lrow[nb] = pair_sum(lsum[nb]) + ((l32 < 16) ? e0 : e1);
   }
   // The fast pass is kept unless some row's probabilities grew so far past its
   // reference that the sums lost range: a row sum above 2^64, or a sum or an
@@ -547,9 +543,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
     __syncthreads();
     const bool redo = (redo_vote[0] | redo_vote[1] | redo_vote[2] | redo_vote[3]) != 0;
     if (redo) {
-      reset(true);
-      issue_tile(kt0, 0);
-      walk(tile_exact, std::true_type{}, kt0, kt1 + 1);
+      reset();
+      issue_tile(kt1, 0);
+      walk(tile_exact, std::true_type{}, kt1, kt0);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) lrow[nb] = pair_sum(lsum[nb]);
     }
