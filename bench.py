@@ -1,6 +1,7 @@
 """Benchmark: prefill attention TFLOP/s (unmasked pairs) on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --sweep            # the chart family: one JSON line per point
 
 One step is one ts_mha_prefill call over the whole workload: every stage of the
 operation (tile walk, QK^T, mask, online softmax with sink, PV, epilogue) runs
@@ -126,6 +127,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration runs)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every chart point (sequence length x batch, full causal) instead")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {a.gpus} is not supported "
@@ -138,47 +141,62 @@ def main():
     import sinks_ts_mha_amd as tm
     from sinks_ts_mha_amd import workloads
 
-    name = a.workload or workloads.DEFAULT_BENCH_WORKLOAD
-    wl = workloads.WORKLOADS[name]
-    inp = workloads.make_inputs(wl)
     dev = torch.device("cuda", 0)
-    q, k, v = inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev)
-    sinks = inp["sinks"].to(dev) if inp["sinks"] is not None else None
-    cu = inp["cu_seqlens"].to(dev)
-    out = torch.empty_like(q)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
-        tm.ts_mha_prefill(q, k, v, sinks, cu, window=wl.window, softmax_scale=wl.softmax_scale,
-                          out=out, max_seqlen=wl.max_seqlen, stream=stream)
+    def timed(wl, steps, warmup, copy_calibration=False):
+        """Resident inputs, W warm-up launches, then K launches timed on the host clock and by
+        one pair of HIP events on the launch stream: (inputs, ms per step, kernel avg ms)."""
+        inp = workloads.make_inputs(wl)
+        q, k, v = inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev)
+        sinks = inp["sinks"].to(dev) if inp["sinks"] is not None else None
+        cu = inp["cu_seqlens"].to(dev)
+        out = torch.empty_like(q)
 
-    if a.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
+        def step():
+            tm.ts_mha_prefill(q, k, v, sinks, cu, window=wl.window, softmax_scale=wl.softmax_scale,
+                              out=out, max_seqlen=wl.max_seqlen, stream=stream)
+
+        if copy_calibration:
+            src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            del src, dst
+        for _ in range(warmup):
+            step()
+        # One event pair on the launch stream around the K back-to-back launches:
+        # the GPU-side span divided by K is the kernel's average launch duration
+        # (events between launches would add their own dispatch gaps).
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        del src, dst
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        del q, k, v, sinks, cu, out
+        return inp, wall * 1e3 / steps, ev0.elapsed_time(ev1) / steps
 
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
+    if a.sweep:
+        for wl in workloads.SWEEP.values():
+            _, ms_step, ms_kernel = timed(wl, a.steps, a.warmup)
+            flops = 4 * wl.head_dim * wl.n_q_heads * tm.ts_mha_unmasked_pairs(wl.cu_seqlens(), 0)
+            print(json.dumps({"sweep_point": wl.name, "batch": len(wl.seqlens), "seq_len": wl.seqlens[0],
+                              "value": round(flops / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                              "kernel_avg_us": round(ms_kernel * 1e3, 2),
+                              "frac": round(flops / (ms_kernel * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                              "steps": a.steps, "warmup": a.warmup}), flush=True)
+            torch.cuda.empty_cache()
+        return
 
-    # One event pair on the launch stream around the K back-to-back launches:
-    # the GPU-side span divided by K is the kernel's average launch duration
-    # (events between launches would add their own dispatch gaps).
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(a.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    avg_ms = ev0.elapsed_time(ev1) / a.steps
-    ms_per_step = wall * 1e3 / a.steps
+    name = a.workload or workloads.DEFAULT_BENCH_WORKLOAD
+    wl = workloads.get(name)
+    inp, ms_per_step, avg_ms = timed(wl, a.steps, a.warmup, a.copy_calibration)
 
     pairs = tm.ts_mha_unmasked_pairs(wl.cu_seqlens(), wl.window)
     flops = 4 * wl.head_dim * wl.n_q_heads * pairs

@@ -78,6 +78,26 @@ WORKLOADS = {
 # The workload a benchmark step runs by default: the full-causal GPT-OSS layer.
 DEFAULT_BENCH_WORKLOAD = "gptoss_full_4x2048"
 
+# The prefill chart family of the same blog post and section: full causal,
+# 64 q / 8 KV heads, head_dim 64, sinks, every sequence of a batch the same
+# length, over sequence length x batch.
+SWEEP_SEQLENS = (1024, 2048, 4096, 8192)
+SWEEP_BATCHES = (1, 2, 4, 8, 16)
+SWEEP = {
+    f"sweep_b{b}_s{n}": Workload(f"sweep_b{b}_s{n}", (n,) * b, 64, 8,
+                                 notes=f"chart point: batch {b} x {n} tokens, full causal, sinks")
+    for n in SWEEP_SEQLENS for b in SWEEP_BATCHES
+}
+
+
+def get(name: str) -> Workload:
+    """A named workload: one of WORKLOADS or a chart point of SWEEP."""
+    if name in WORKLOADS:
+        return WORKLOADS[name]
+    if name in SWEEP:
+        return SWEEP[name]
+    raise KeyError(f"unknown workload {name!r}")
+
 
 def make_inputs(wl: Workload, seed: int | None = None, device: str = "cpu") -> dict:
     """Draw q, k, v (bf16) and sinks (fp32) for a workload; see the module recipe."""

@@ -93,3 +93,28 @@ def test_long_prefill_sampled_rows(oracle_lib):
     heads = np.tile(np.arange(wl.n_q_heads), pos.size)
     ref = oracle.prefill_rows(*oracle_args(inp), rows=rows, heads=heads, lib=oracle_lib)
     check(got[rows, heads], ref, "long_1x32768 sampled")
+
+
+SWEEP_CASES = ["sweep_b16_s1024", "sweep_b2_s4096", "sweep_b1_s8192", "sweep_b16_s8192"]
+
+
+@pytest.mark.parametrize("name", SWEEP_CASES)
+def test_chart_point_sampled_rows(name, oracle_lib):
+    """Points of the chart family (sequence length x batch, full causal), at their real sizes:
+    in every sequence the first 64 positions, the last 32 and every 257th, every query head."""
+    wl = workloads.get(name)
+    inp = workloads.make_inputs(wl)
+    say(f"chart point {name} T={wl.total_tokens}")
+    got = f64(run_gpu(inp).cpu())
+    torch.cuda.synchronize()
+    cu = wl.cu_seqlens().tolist()
+    pos = []
+    for b in range(len(cu) - 1):
+        L = cu[b + 1] - cu[b]
+        rel = np.unique(np.concatenate([np.arange(64), np.arange(L - 32, L), np.arange(0, L, 257)]))
+        pos.append(cu[b] + rel)
+    pos = np.concatenate(pos)
+    rows = np.repeat(pos, wl.n_q_heads)
+    heads = np.tile(np.arange(wl.n_q_heads), pos.size)
+    ref = oracle.prefill_rows(*oracle_args(inp), rows=rows, heads=heads, lib=oracle_lib)
+    check(got[rows, heads], ref, f"{name} sampled")
