@@ -210,6 +210,11 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   const int p0 = pblk * P;
   if (p0 >= L) return;
 
+  // The prologue (address set-up and the first loads) runs at raised wave
+  // priority: a work-group starting next to a busy one on its compute unit
+  // would otherwise issue only in that one's gaps.  The tile walk runs at the
+  // normal priority.
+  __builtin_amdgcn_s_setprio(2);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -511,6 +516,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   };
 
   reset();
+  __builtin_amdgcn_s_setprio(0);
   walk(tile_exact, std::true_type{}, kt1, ktB);
   walk(tile_fast, std::false_type{}, ktB - 1, ktA);
   if constexpr (WINDOWED) walk(tile_fast, std::true_type{}, ktA - 1, kt0);
