@@ -47,7 +47,10 @@ extern "C" {
 #define TS_MHA_OK 0
 #define TS_MHA_ERR_NULL_ARG (-1)     /* a required pointer is NULL */
 #define TS_MHA_ERR_BAD_SHAPE (-2)    /* heads <= 0, n_q_heads % n_kv_heads != 0, n_seqs < 0,
-                                        max_seqlen < 0, or the launch grid would overflow */
+                                        max_seqlen < 0, the launch grid would overflow, or one
+                                        sequence's q rows ((max_seqlen + 256) * n_q_heads * 128
+                                        bytes) or k/v rows ((max_seqlen + 64) * n_kv_heads * 128
+                                        bytes) would exceed 2^31 - 1 bytes */
 #define TS_MHA_ERR_UNSUPPORTED (-3)  /* head_dim != 64, or n_q_heads / n_kv_heads not in {1,2,4,8,16} */
 #define TS_MHA_ERR_BAD_SCALE (-4)    /* softmax_scale not finite or <= 0 */
 #define TS_MHA_ERR_ALIGN (-5)        /* q, k, v or out not 16-byte aligned; sinks or cu_seqlens not 4-byte aligned */

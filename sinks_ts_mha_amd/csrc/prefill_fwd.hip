@@ -192,6 +192,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   constexpr int P = kRows / G;  // positions per work-group
   __shared__ u32x4 lds_k[kSlots * kTileChunks];
   __shared__ u32x4 lds_v[kSlots * kTileChunks];
+  __shared__ u32x4 lds_q[kRows * kChunks];  // the work-group's query rows, staged once
   __shared__ int redo_vote[kWaves];
 
   const int Hkv = p.n_kv_heads;
@@ -277,19 +278,32 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
     head[nb] = g * G + r % G;
     pos[nb] = p0 + r / G;
     sink_t[nb] = p.sinks ? p.sinks[head[nb]] * kLog2e : -INFINITY;
-    if (pos[nb] < L) {
-      const uint16_t* qrow = p.q + ((int64_t)(s + pos[nb]) * Hq + head[nb]) * kD + 8 * hi;
+  }
+  // The query rows go through LDS with the same wave-wide loads as K and V:
+  // each 1 KiB load covers 8 whole rows (the G heads of a position are
+  // contiguous), so it is fully coalesced, and rows past the sequence end
+  // read as zeros.  Wave w loads its own 64 rows, in the layout of a K tile,
+  // and reads them back as MFMA B operands.
+  {
+    const i32x4 rq = buffer_rsrc(p.q + (int64_t)s * Hq * kD, L * Hq * kRowBytes);
+    const uint32_t lds_q_base = lds_addr(lds_q) + w * 64 * kRowBytes;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        qf[nb][ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * ks));
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qf[nb][ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+    for (int it = 0; it < 8; ++it) {
+      const int row = 8 * it + (lane >> 3);  // within the wave's 64 rows
+      const int r = 64 * w + row;
+      const int data_ch = (lane & 7) ^ swz_key(row);
+      lds_dma16(lds_q_base + it * 1024, rq, ((p0 + r / G) * Hq + g * G + r % G) * kRowBytes + data_ch * 16);
     }
   }
-  // The Q loads above (and the first tile's) complete here, not inside the
+  wait_vmem<0>();  // the query rows (and the first tile) have landed in LDS
+  // The first tile's loads and the query loads complete here, not inside the
   // tile loop.
   __builtin_amdgcn_s_waitcnt(0x0F70);
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qf[nb][ks] = __builtin_bit_cast(bf16x8, lds_q[w * 64 * kChunks + swz(32 * nb + l32, 2 * ks + hi)]);
 
   // K fragments (A operand) of key half mb for the four 16-wide steps of head_dim.
   // Per-lane byte offsets of the operand reads within a tile, fixed for the
@@ -601,6 +615,8 @@ int64_t pblocks(const PrefillArgs& a) {
 int64_t prefill_grid_size(const PrefillArgs& a) {
   // each sequence's K (or V) rows must be addressable by one buffer descriptor
   if (((int64_t)a.max_seqlen + kBK) * a.n_kv_heads * kRowBytes > 0x7fffffffLL) return -1;
+  // and its query rows, including a position block's rows past the end
+  if (((int64_t)a.max_seqlen + kRows) * a.n_q_heads * kRowBytes > 0x7fffffffLL) return -1;
   const int64_t n = pblocks(a) * (int64_t)a.n_seqs * (int64_t)a.n_kv_heads;
   if (n > 0x7fffffffLL) return -1;
   return n;

@@ -56,6 +56,10 @@ def call(q=FAKE, k=FAKE, v=FAKE, sinks=None, cu=FAKE, hq=64, hkv=8, d=64, window
     (dict(hq=0), -2), (dict(hkv=0), -2), (dict(hq=-8), -2), (dict(hq=12, hkv=8), -2),
     (dict(n_seqs=-1), -2), (dict(max_seqlen=-5), -2),
     (dict(max_seqlen=2**31 - 1, n_seqs=2**20), -2),
+    # one sequence's q rows beyond 2^31 - 1 bytes: (262000 + 256) * 64 heads * 128 B
+    (dict(max_seqlen=262000, n_seqs=1), -2),
+    # its k/v rows beyond 2^31 - 1 bytes with few q heads: (2**21 + 64) * 8 * 128 B
+    (dict(max_seqlen=2**21, hq=8, hkv=8, n_seqs=1), -2),
     (dict(d=128), -3), (dict(d=32), -3), (dict(hq=24, hkv=8), -3), (dict(hq=64, hkv=2), -3),
     (dict(scale=0.0), -4), (dict(scale=-0.1), -4), (dict(scale=float("nan")), -4),
     (dict(scale=float("inf")), -4),
@@ -74,6 +78,7 @@ def test_validation_precedes_device_check():
     assert call() == -6
     assert call(window=128, sinks=FAKE) == -6
     assert call(n_seqs=0, max_seqlen=0) == -6
+    assert call(max_seqlen=261000, n_seqs=1) == -6  # just inside the q-row limit
 
 
 def test_strerror_texts():
