@@ -7,8 +7,11 @@ imports it.
 
 Inputs are numpy arrays: q, k, v as uint16 bf16 bit patterns in the packed
 layout [T, heads, head_dim]; sinks as float32 [n_q_heads] or None; cu_seqlens
-as int32 [n_seqs + 1].  Outputs are float64.  The arithmetic lives in the C
-file; see its header for what is computed and which pages it follows.
+as int32 [n_seqs + 1].  The cache form (cache_attend) takes k_cache / v_cache
+as uint16 [n_pages, page_size, n_kv_heads, head_dim], seqlens_k as int32
+[n_seqs] and block_table as int32 [n_seqs, pages_per_seq].  Outputs are
+float64.  The arithmetic lives in the C file; see its header for what is
+computed and which pages it follows.
 """
 from __future__ import annotations
 
@@ -57,6 +60,11 @@ def load(path: str = _LIB, build_if_missing: bool = True):
     lib.ts_oracle_prefill_rows.restype = ctypes.c_int
     lib.ts_oracle_row_probs.argtypes = common + [ctypes.c_int64, ctypes.c_int32, f64p, f64p]
     lib.ts_oracle_row_probs.restype = ctypes.c_int
+    lib.ts_oracle_cache.argtypes = [u16p, u16p, u16p, f32p, i32p, i32p, i32p, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
+                                    i64p, i32p, ctypes.c_int64, f64p]
+    lib.ts_oracle_cache.restype = ctypes.c_int
     if path == _LIB:
         _lib = lib
     return lib
@@ -134,3 +142,50 @@ def row_probs(q, k, v, sinks, cu_seqlens, window: int, scale: float, row: int, h
                                    int(head), _ptr(probs, ctypes.c_double),
                                    ctypes.byref(p_sink)), "ts_oracle_row_probs")
     return probs, p_sink.value
+
+
+def cache_attend(q, k_cache, v_cache, sinks, cu_seqlens_q, seqlens_k, block_table, window: int,
+                 scale: float, rows=None, heads=None, lib=None) -> np.ndarray:
+    """New query rows against a paged KV cache (prefill with a cache; decode is q_len = 1).
+
+    Row i of sequence b's q_len rows sits at position seqlens_k[b] - q_len + i.
+    Returns float64 [Tq, n_q_heads, head_dim], or [n, head_dim] for the selected
+    (rows[n], heads[n]).
+    """
+    lib = lib or load()
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    kc = np.ascontiguousarray(k_cache, dtype=np.uint16)
+    vc = np.ascontiguousarray(v_cache, dtype=np.uint16)
+    cu = np.ascontiguousarray(cu_seqlens_q, dtype=np.int32)
+    sk = np.ascontiguousarray(seqlens_k, dtype=np.int32)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    s = None if sinks is None else np.ascontiguousarray(sinks, dtype=np.float32)
+    if q.ndim != 3 or kc.ndim != 4 or kc.shape != vc.shape or kc.shape[3] != q.shape[2]:
+        raise ValueError("q must be [Tq, Hq, D] and k/v caches [n_pages, page_size, Hkv, D]")
+    if cu.ndim != 1 or cu.shape[0] < 1 or int(cu[-1]) != q.shape[0]:
+        raise ValueError("cu_seqlens_q must be [n_seqs + 1] ending at Tq")
+    n_seqs = cu.shape[0] - 1
+    if sk.shape != (n_seqs,) or bt.ndim != 2 or bt.shape[0] != n_seqs:
+        raise ValueError("seqlens_k must be [n_seqs] and block_table [n_seqs, pages_per_seq]")
+    if s is not None and s.shape != (q.shape[1],):
+        raise ValueError("sinks must be [n_q_heads]")
+    hq, D = q.shape[1], q.shape[2]
+    if rows is None:
+        r = h = None
+        out = np.zeros(q.shape, dtype=np.float64)
+        n = 0
+    else:
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        h = np.ascontiguousarray(heads, dtype=np.int32)
+        if r.shape != h.shape or r.ndim != 1:
+            raise ValueError("rows and heads must be 1-D and of equal length")
+        out = np.zeros((r.shape[0], D), dtype=np.float64)
+        n = r.shape[0]
+    _check(lib.ts_oracle_cache(_ptr(q, ctypes.c_uint16), _ptr(kc, ctypes.c_uint16),
+                               _ptr(vc, ctypes.c_uint16), _ptr(s, ctypes.c_float),
+                               _ptr(cu, ctypes.c_int32), _ptr(sk, ctypes.c_int32),
+                               _ptr(bt, ctypes.c_int32), n_seqs, kc.shape[0], kc.shape[1],
+                               bt.shape[1], hq, kc.shape[2], D, int(window), float(scale),
+                               _ptr(r, ctypes.c_int64), _ptr(h, ctypes.c_int32), n,
+                               _ptr(out, ctypes.c_double)), "ts_oracle_cache")
+    return out

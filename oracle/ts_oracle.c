@@ -240,3 +240,125 @@ int ts_oracle_row_probs(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   free(acc);
   return TS_ORACLE_OK;
 }
+
+/* ------------------------------------------------------------------------
+ * Attention of new query rows against a paged KV cache.
+ *
+ * Pages followed: TokenSpeed-kernel README, section "Public API", which lists
+ * `mha_prefill_with_kvcache` and `mha_decode_with_kvcache` beside
+ * `mha_prefill`; "TokenSpeed-kernel multi-silicon" (aixai.ru blog), section
+ * "Архитектура: три слоя", where the runtime's attention calls are prefill and
+ * decode with a KV cache.  The pages print no signature; the readings taken:
+ *  - the cache holds every key and value of a sequence, the new tokens' own
+ *    included (the caller writes them before the call); seqlens_k[b] counts
+ *    them all;
+ *  - layout: k_cache / v_cache [n_pages][page_size][n_kv_heads][D]; key
+ *    position j of sequence b lives in page block_table[b][j / page_size],
+ *    slot j % page_size;
+ *  - the q_len = cu_seqlens_q[b+1] - cu_seqlens_q[b] new query rows are the
+ *    last q_len positions of the sequence: row i sits at position
+ *    p = seqlens_k[b] - q_len + i (the causal diagonal aligned to the bottom
+ *    right); decode is q_len = 1;
+ *  - visible keys, sink, scale and GQA mapping as in the prefill above, with
+ *    p in place of i; a row with p < 0 (fewer cached keys than new rows) sees
+ *    no key and its output is zero.
+ * ------------------------------------------------------------------------ */
+
+/* One output row of the cache form; z holds at least p+1 doubles. */
+static int cache_row(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                     const float* sinks, const int32_t* block_table, int32_t b, int64_t p,
+                     int64_t t, int32_t h, int32_t n_pages, int32_t page_size,
+                     int32_t pages_per_seq, int32_t n_q_heads, int32_t n_kv_heads,
+                     int32_t head_dim, int32_t window, double scale, double* z, double* acc,
+                     double* out_row) {
+  const int32_t G = n_q_heads / n_kv_heads;
+  const int32_t g = h / G;
+  for (int32_t d = 0; d < head_dim; ++d) out_row[d] = 0.0;
+  if (p < 0) return TS_ORACLE_OK;
+  const int64_t jlo = first_visible(p, window);
+  const double sigma = sinks ? (double)sinks[h] : -INFINITY;
+  const uint16_t* qrow = q + (t * n_q_heads + h) * (int64_t)head_dim;
+  const int32_t* pages = block_table + (int64_t)b * pages_per_seq;
+
+  /* pass 1: scaled scores and the maximum, sink included */
+  double m = sigma;
+  for (int64_t j = jlo; j <= p; ++j) {
+    const int64_t slot = j % page_size;
+    const int64_t pi = j / page_size;
+    if (pi >= pages_per_seq || pages[pi] < 0 || pages[pi] >= n_pages) return TS_ORACLE_BAD_ARGS;
+    const uint16_t* krow = k_cache + (((int64_t)pages[pi] * page_size + slot) * n_kv_heads + g) * head_dim;
+    double dot = 0.0;
+    for (int32_t d = 0; d < head_dim; ++d)
+      dot += bf16_to_double(qrow[d]) * bf16_to_double(krow[d]);
+    z[j - jlo] = scale * dot;
+    if (z[j - jlo] > m) m = z[j - jlo];
+  }
+
+  /* pass 2: exponentials, denominator (sink term first), weighted sum of V rows */
+  double den = sinks ? exp(sigma - m) : 0.0;
+  for (int32_t d = 0; d < head_dim; ++d) acc[d] = 0.0;
+  for (int64_t j = jlo; j <= p; ++j) {
+    const double w = exp(z[j - jlo] - m);
+    const uint16_t* vrow = v_cache + (((int64_t)pages[j / page_size] * page_size + j % page_size) * n_kv_heads + g) * head_dim;
+    den += w;
+    for (int32_t d = 0; d < head_dim; ++d) acc[d] += w * bf16_to_double(vrow[d]);
+  }
+  for (int32_t d = 0; d < head_dim; ++d) out_row[d] = acc[d] / den;
+  return TS_ORACLE_OK;
+}
+
+/* Rows of the cache form.  q and out are packed [Tq][n_q_heads][D] by
+ * cu_seqlens_q (Tq = cu_seqlens_q[n_seqs]).  With rows == NULL every
+ * (row, head) is computed into out[Tq][n_q_heads][D]; otherwise row n is
+ * (packed row rows[n], head heads[n]) into out[n][D]. */
+int ts_oracle_cache(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                    const float* sinks, const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                    const int32_t* block_table, int32_t n_seqs, int32_t n_pages,
+                    int32_t page_size, int32_t pages_per_seq, int32_t n_q_heads,
+                    int32_t n_kv_heads, int32_t head_dim, int32_t window, double scale,
+                    const int64_t* rows, const int32_t* heads, int64_t n_rows, double* out) {
+  int rc = check_args(q, k_cache, v_cache, cu_seqlens_q, n_seqs, n_q_heads, n_kv_heads, head_dim, scale);
+  if (rc) return rc;
+  if (!seqlens_k || n_pages < 0 || page_size <= 0 || pages_per_seq < 0) return TS_ORACLE_BAD_ARGS;
+  int64_t max_len = 1;
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    if (seqlens_k[b] < 0 || (int64_t)seqlens_k[b] > (int64_t)pages_per_seq * page_size) return TS_ORACLE_BAD_ARGS;
+    if (seqlens_k[b] > max_len) max_len = seqlens_k[b];
+  }
+  if (n_seqs > 0 && pages_per_seq > 0 && !block_table) return TS_ORACLE_BAD_ARGS;
+  const int64_t Tq = cu_seqlens_q[n_seqs];
+  const int64_t n = rows ? n_rows : Tq * n_q_heads;
+  if (n < 0 || (n > 0 && !out) || (rows && n > 0 && !heads)) return TS_ORACLE_BAD_ARGS;
+  if (rows)
+    for (int64_t r = 0; r < n; ++r)
+      if (rows[r] < 0 || rows[r] >= Tq || heads[r] < 0 || heads[r] >= n_q_heads) return TS_ORACLE_BAD_ARGS;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* z = (double*)malloc(sizeof(double) * (size_t)max_len);
+    double* acc = (double*)malloc(sizeof(double) * (size_t)head_dim);
+    if (!z || !acc) {
+#pragma omp atomic write
+      failed = TS_ORACLE_NO_MEMORY;
+    } else {
+#pragma omp for schedule(dynamic, 4)
+      for (int64_t r = 0; r < n; ++r) {
+        const int64_t t = rows ? rows[r] : r / n_q_heads;
+        const int32_t h = rows ? heads[r] : (int32_t)(r % n_q_heads);
+        const int32_t b = seq_of_row(cu_seqlens_q, n_seqs, t);
+        const int64_t q_len = cu_seqlens_q[b + 1] - cu_seqlens_q[b];
+        const int64_t p = (int64_t)seqlens_k[b] - q_len + (t - cu_seqlens_q[b]);
+        const int rr = cache_row(q, k_cache, v_cache, sinks, block_table, b, p, t, h, n_pages,
+                                 page_size, pages_per_seq, n_q_heads, n_kv_heads, head_dim, window,
+                                 scale, z, acc, out + r * (int64_t)head_dim);
+        if (rr) {
+#pragma omp atomic write
+          failed = rr;
+        }
+      }
+    }
+    free(z);
+    free(acc);
+  }
+  return failed;
+}

@@ -15,6 +15,16 @@ Recipe (identical bits reach the oracle and the GPU):
   one CPU torch.Generator seeded with `seed` draws, in this order,
   q [T, Hq, D], k [T, Hkv, D], v [T, Hkv, D], sinks [Hq] as float32 N(0, 1);
   q, k, v are then rounded to bfloat16 (round to nearest even).
+
+Paged-cache workloads (decode, and prefill of new rows against a cache): the
+generator draws q [Tq, Hq, D], k_cache and v_cache [n_pages, page_size, Hkv, D],
+sinks [Hq] as float32 N(0, 1), then a random permutation of the page ids; the
+sequences take consecutive runs of that permutation, ceil(k_len / page_size)
+pages each, and the block table rows are padded with -1.  The pool holds
+`spare_pages` more pages than the sequences use.  The decode shapes follow the
+GPT-OSS layers of the same pages (64 q / 8 KV heads, head_dim 64, sinks, full and
+window-128 layers); the pages give no decode batch or context length, so the
+benchmark takes batch 64 at 8K context and batch 1 at 64K.
 """
 from __future__ import annotations
 
@@ -90,12 +100,14 @@ SWEEP = {
 }
 
 
-def get(name: str) -> Workload:
-    """A named workload: one of WORKLOADS or a chart point of SWEEP."""
+def get(name: str):
+    """A named workload: one of WORKLOADS, a chart point of SWEEP, or a CACHE_WORKLOADS entry."""
     if name in WORKLOADS:
         return WORKLOADS[name]
     if name in SWEEP:
         return SWEEP[name]
+    if name in CACHE_WORKLOADS:
+        return CACHE_WORKLOADS[name]
     raise KeyError(f"unknown workload {name!r}")
 
 
@@ -122,6 +134,106 @@ def make_inputs(wl: Workload, seed: int | None = None, device: str = "cpu") -> d
         out = {key: (val.to(device) if isinstance(val, torch.Tensor) else val)
                for key, val in out.items()}
     return out
+
+
+@dataclass(frozen=True)
+class CacheWorkload:
+    """New query rows against a paged KV cache; decode when every q_len is 1."""
+    name: str
+    q_lens: tuple              # new query rows per sequence
+    k_lens: tuple              # cached keys per sequence, the new rows' own included
+    n_q_heads: int
+    n_kv_heads: int
+    page_size: int = 16
+    head_dim: int = 64
+    window: int = 0
+    sinks: bool = True
+    softmax_scale: float = 0.125
+    seed: int = 0
+    spare_pages: int = 3
+    notes: str = field(default="", compare=False)
+
+    @property
+    def n_seqs(self) -> int:
+        return len(self.k_lens)
+
+    @property
+    def total_q(self) -> int:
+        return int(sum(self.q_lens))
+
+    @property
+    def max_seqlen_k(self) -> int:
+        return int(max(self.k_lens)) if self.k_lens else 0
+
+    @property
+    def max_seqlen_q(self) -> int:
+        return int(max(self.q_lens)) if self.q_lens else 0
+
+    @property
+    def pages_per_seq(self) -> int:
+        return max(1, -(-self.max_seqlen_k // self.page_size))
+
+    @property
+    def n_pages(self) -> int:
+        return sum(-(-int(n) // self.page_size) for n in self.k_lens) + self.spare_pages
+
+    def cu_seqlens_q(self) -> torch.Tensor:
+        cu = [0]
+        for n in self.q_lens:
+            cu.append(cu[-1] + int(n))
+        return torch.tensor(cu, dtype=torch.int32)
+
+
+def decode(k_lens, n_q_heads=64, n_kv_heads=8, window=0, page_size=16, sinks=True, seed=0,
+           name="decode", **kw) -> CacheWorkload:
+    k_lens = tuple(int(x) for x in k_lens)
+    return CacheWorkload(name, (1,) * len(k_lens), k_lens, n_q_heads, n_kv_heads, page_size,
+                         window=window, sinks=sinks, seed=seed, **kw)
+
+
+CACHE_WORKLOADS = {
+    "decode_b64_k8192": decode(
+        (8192,) * 64, name="decode_b64_k8192",
+        notes="GPT-OSS full layer, decode: 64 sequences x 8192 cached keys, page 16, sinks"),
+    "decode_b64_k8192_window128": decode(
+        (8192,) * 64, window=128, name="decode_b64_k8192_window128",
+        notes="GPT-OSS sliding-window layer, decode: 64 x 8192 cached keys, window 128, page 16"),
+    "decode_b1_k65536": decode(
+        (65536,), name="decode_b1_k65536",
+        notes="one long sequence, decode: 65536 cached keys, page 16, sinks"),
+}
+
+
+def make_cache_inputs(wl: CacheWorkload, seed: int | None = None) -> dict:
+    """Draw q, the paged k/v caches, sinks and the block table; see the module recipe."""
+    seed = wl.seed if seed is None else seed
+    D, P = wl.head_dim, wl.page_size
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((wl.total_q, wl.n_q_heads, D), generator=g, dtype=torch.float32)
+    kc = torch.randn((wl.n_pages, P, wl.n_kv_heads, D), generator=g, dtype=torch.float32)
+    vc = torch.randn((wl.n_pages, P, wl.n_kv_heads, D), generator=g, dtype=torch.float32)
+    sinks = torch.randn((wl.n_q_heads,), generator=g, dtype=torch.float32)
+    perm = torch.randperm(wl.n_pages, generator=g)
+    table = torch.full((wl.n_seqs, wl.pages_per_seq), -1, dtype=torch.int32)
+    nxt = 0
+    for b, n in enumerate(wl.k_lens):
+        need = -(-int(n) // P)
+        table[b, :need] = perm[nxt:nxt + need].to(torch.int32)
+        nxt += need
+    return {
+        "q": q.to(torch.bfloat16),
+        "k_cache": kc.to(torch.bfloat16),
+        "v_cache": vc.to(torch.bfloat16),
+        "sinks": sinks if wl.sinks else None,
+        "cu_seqlens_q": wl.cu_seqlens_q(),
+        "seqlens_k": torch.tensor(wl.k_lens, dtype=torch.int32),
+        "block_table": table,
+        "max_seqlen_q": wl.max_seqlen_q,
+        "max_seqlen_k": wl.max_seqlen_k,
+        "page_size": P,
+        "window": wl.window,
+        "softmax_scale": wl.softmax_scale,
+    }
 
 
 def custom(seqlens, n_q_heads, n_kv_heads, window=0, sinks=True, head_dim=64,

@@ -31,6 +31,7 @@ import torch.nn.functional as F
 from oracle import oracle
 from sinks_ts_mha_amd import workloads
 from _util import oracle_args
+from sinks_ts_mha_amd.workloads import bf16_bits
 
 
 def _run(lib, inp):
@@ -305,3 +306,158 @@ ALL_PINS = [pin_sdpa_no_sink, pin_sdpa_sink_augmented, pin_closed_form_q_zero,
             pin_closed_form_window_one, pin_hand_example, pin_sink_extremes,
             pin_probs_sum_to_one, pin_window_covering_equals_full, pin_packed_equals_separate,
             pin_permute_sequences, pin_causality, pin_head_groups, pin_scale_homogeneity]
+
+
+# ---------------------------------------------------------------------------
+# Pins of the paged-cache form (oracle.cache_attend): new query rows against a
+# KV cache, the causal diagonal aligned to the bottom right; decode is q_len 1.
+
+def _cache_inputs(q_lens, k_lens, hq, hkv, page_size, window=0, sinks=True, seed=0, spare=3):
+    wl = workloads.CacheWorkload("pin", tuple(q_lens), tuple(k_lens), hq, hkv, page_size,
+                                 window=window, sinks=sinks, seed=seed, spare_pages=spare)
+    return workloads.make_cache_inputs(wl)
+
+
+def _cache_run(lib, inp):
+    return oracle.cache_attend(
+        bf16_bits(inp["q"]), bf16_bits(inp["k_cache"]), bf16_bits(inp["v_cache"]),
+        None if inp["sinks"] is None else inp["sinks"].numpy().astype(np.float32),
+        inp["cu_seqlens_q"].numpy(), inp["seqlens_k"].numpy(), inp["block_table"].numpy(),
+        inp["window"], inp["softmax_scale"], lib=lib)
+
+
+def _gather(cache, table_row, L, page_size):
+    """Contiguous [L, Hkv, D] rows of one sequence, fetched page by page."""
+    rows = [cache[int(table_row[j // page_size]), j % page_size] for j in range(L)]
+    return torch.stack(rows) if rows else cache[0, :0]
+
+
+def _cache_sdpa_reference(inp, augment_sink: bool):
+    """SDPA in float64 per sequence on gathered K/V, mask aligned to the bottom right."""
+    q = inp["q"].to(torch.float64)
+    hq, D = q.shape[1], q.shape[2]
+    hkv = inp["k_cache"].shape[2]
+    G = hq // hkv
+    P = inp["page_size"]
+    scale, W = inp["softmax_scale"], inp["window"]
+    cu = inp["cu_seqlens_q"].tolist()
+    out = torch.zeros_like(q)
+    for b in range(len(cu) - 1):
+        qs, qe = cu[b], cu[b + 1]
+        nq, L = qe - qs, int(inp["seqlens_k"][b])
+        if nq == 0:
+            continue
+        k = _gather(inp["k_cache"], inp["block_table"][b], L, P).to(torch.float64)
+        v = _gather(inp["v_cache"], inp["block_table"][b], L, P).to(torch.float64)
+        pos = torch.arange(nq).view(nq, 1) + (L - nq)
+        j = torch.arange(L).view(1, L)
+        mask = (j <= pos) & ((pos - j < W) if W > 0 else torch.ones_like(j, dtype=torch.bool))
+        qb = q[qs:qe].transpose(0, 1)
+        kb = k.repeat_interleave(G, dim=1).transpose(0, 1)
+        vb = v.repeat_interleave(G, dim=1).transpose(0, 1)
+        if augment_sink:
+            sig = inp["sinks"].to(torch.float64)
+            qb = torch.cat([qb, torch.ones(hq, nq, 1, dtype=torch.float64)], dim=2)
+            kb = torch.cat([kb, torch.zeros(hq, L, 1, dtype=torch.float64)], dim=2)
+            ksink = torch.zeros(hq, 1, D + 1, dtype=torch.float64)
+            ksink[:, 0, D] = sig / scale
+            kb = torch.cat([kb, ksink], dim=1)
+            vb = torch.cat([vb, torch.zeros(hq, 1, D, dtype=torch.float64)], dim=1)
+            mask = torch.cat([mask, torch.ones(nq, 1, dtype=torch.bool)], dim=1)
+        ob = F.scaled_dot_product_attention(qb.contiguous(), kb.contiguous(), vb.contiguous(),
+                                            attn_mask=mask, scale=scale)
+        # a row that sees no key has no softmax; its output is zero by definition
+        ob = torch.where(mask.any(dim=1).view(1, nq, 1), ob, torch.zeros_like(ob))
+        out[qs:qe] = ob.transpose(0, 1)
+    return out.numpy()
+
+
+CACHE_CASES = [  # (q_lens, k_lens, Hq, Hkv, page_size, window)
+    ([1, 1, 1, 1], [1, 9, 40, 17], 4, 2, 4, 0),
+    ([3, 1, 7], [3, 30, 50], 4, 1, 8, 0),
+    ([5, 2], [44, 13], 8, 2, 4, 6),
+    ([1, 1], [64, 33], 2, 2, 16, 1),
+    ([12], [12], 4, 2, 4, 5),
+    ([0, 4, 1], [10, 4, 0], 4, 2, 2, 0),
+]
+
+
+def pin_cache_sdpa(lib):
+    for n, (ql, kl, hq, hkv, P, w) in enumerate(CACHE_CASES):
+        for with_sink in (False, True):
+            inp = _cache_inputs(ql, kl, hq, hkv, P, window=w, sinks=with_sink, seed=200 + n)
+            if with_sink:
+                inp["sinks"] = inp["sinks"] * 3.0 + torch.linspace(-2.0, 4.0, hq)
+            _close(_cache_run(lib, inp), _cache_sdpa_reference(inp, with_sink), 1e-12,
+                   f"cache SDPA case q_lens={ql} k_lens={kl} page={P} W={w} sink={with_sink}")
+
+
+def _contiguous_prefill_inputs(inp):
+    """The same sequences as plain packed prefill inputs (q_len == k_len for each)."""
+    P = inp["page_size"]
+    ks, vs = [], []
+    for b in range(inp["seqlens_k"].shape[0]):
+        L = int(inp["seqlens_k"][b])
+        ks.append(_gather(inp["k_cache"], inp["block_table"][b], L, P))
+        vs.append(_gather(inp["v_cache"], inp["block_table"][b], L, P))
+    return {"q": inp["q"], "k": torch.cat(ks), "v": torch.cat(vs), "sinks": inp["sinks"],
+            "cu_seqlens": inp["cu_seqlens_q"], "window": inp["window"],
+            "softmax_scale": inp["softmax_scale"]}
+
+
+def pin_cache_full_chunk_is_prefill(lib):
+    """When the new rows are the whole sequence, the cache form is the plain prefill."""
+    for n, (lens, P, w) in enumerate([([7, 33, 1], 4, 0), ([20, 48], 16, 9), ([0, 5], 2, 2)]):
+        inp = _cache_inputs(lens, lens, 4, 2, P, window=w, seed=220 + n)
+        _close(_cache_run(lib, inp), _run(lib, _contiguous_prefill_inputs(inp)), 1e-13,
+               f"full chunk vs prefill lens={lens} page={P} W={w}")
+
+
+def pin_cache_decode_is_last_prefill_row(lib):
+    """Decode of position i (q_len 1, k_len i + 1) equals row i of the full prefill."""
+    L, P = 37, 8
+    for w in (0, 10):
+        full = _cache_inputs([L], [L], 4, 2, P, window=w, seed=240 + w)
+        ref = _run(lib, _contiguous_prefill_inputs(full))
+        for i in (0, 1, 9, 10, 24, L - 1):
+            one = dict(full, q=full["q"][i:i + 1],
+                       cu_seqlens_q=torch.tensor([0, 1], dtype=torch.int32),
+                       seqlens_k=torch.tensor([i + 1], dtype=torch.int32))
+            _close(_cache_run(lib, one), ref[i:i + 1], 1e-13, f"decode at position {i}, W={w}")
+
+
+def pin_cache_page_layout(lib):
+    """Where the pages sit in the pool, and what unused slots hold, does not matter."""
+    inp = _cache_inputs([2, 1, 4], [19, 26, 9], 4, 2, 4, window=0, seed=260, spare=5)
+    base = _cache_run(lib, inp)
+    n_pages = inp["k_cache"].shape[0]
+    perm = torch.randperm(n_pages, generator=torch.Generator().manual_seed(7))
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(n_pages)
+    table = inp["block_table"].clone()
+    table[table >= 0] = inv[table[table >= 0].long()].to(torch.int32)
+    moved = dict(inp, k_cache=inp["k_cache"][perm], v_cache=inp["v_cache"][perm], block_table=table)
+    assert np.array_equal(_cache_run(lib, moved), base), "moving pages changed the result"
+    # poison every slot no sequence uses
+    used = torch.zeros(n_pages, inp["page_size"], dtype=torch.bool)
+    for b in range(3):
+        for j in range(int(inp["seqlens_k"][b])):
+            used[int(inp["block_table"][b, j // 4]), j % 4] = True
+    kc, vc = inp["k_cache"].clone(), inp["v_cache"].clone()
+    kc[~used] = float("nan")
+    vc[~used] = float("nan")
+    poisoned = _cache_run(lib, dict(inp, k_cache=kc, v_cache=vc))
+    assert np.array_equal(poisoned, base), "unused cache slots leaked into the result"
+
+
+def pin_cache_rows_without_keys(lib):
+    """A row with no cached key at or before its position has a zero output."""
+    inp = _cache_inputs([3, 1, 2], [1, 0, 2], 4, 2, 4, seed=280)
+    out = _cache_run(lib, inp)
+    assert np.all(out[0:2] == 0.0) and np.any(out[2] != 0.0), "rows before the first key"
+    assert np.all(out[3] == 0.0), "empty sequence"
+    assert np.all(out[4:6] != 0.0)
+
+
+ALL_PINS += [pin_cache_sdpa, pin_cache_full_chunk_is_prefill, pin_cache_decode_is_last_prefill_row,
+             pin_cache_page_layout, pin_cache_rows_without_keys]

@@ -14,7 +14,7 @@ from oracle_pins import ALL_PINS
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ts_oracle.c")
 
 # (name, original, replacement[, original, replacement ...]) -- every original must
-# occur in the source.
+# occur in the source; the first occurrence is the one replaced.
 MUTANTS = [
     ("sink_dropped_from_denominator",
      "double den = (sigma == -INFINITY) ? 0.0 : exp(sigma - m);", "double den = 0.0;"),
@@ -46,6 +46,19 @@ MUTANTS = [
     ("sink_share_unshifted", "*p_sink = (sigma == -INFINITY) ? 0.0 : exp(sigma - m) / den;",
      "*p_sink = (sigma == -INFINITY) ? 0.0 : exp(sigma) / den;"),
     ("bf16_widening_wrong_half", "uint32_t w = ((uint32_t)bits) << 16;", "uint32_t w = ((uint32_t)bits) << 15;"),
+    # the paged-cache form
+    ("cache_top_left_alignment",
+     "const int64_t p = (int64_t)seqlens_k[b] - q_len + (t - cu_seqlens_q[b]);",
+     "const int64_t p = t - cu_seqlens_q[b];"),
+    ("cache_table_row_ignored", "const int32_t* pages = block_table + (int64_t)b * pages_per_seq;",
+     "const int32_t* pages = block_table;"),
+    ("cache_window_off_by_one", "const int64_t jlo = first_visible(p, window);",
+     "const int64_t jlo = first_visible(p + 1, window);"),
+    ("cache_value_from_key_cache", "const uint16_t* vrow = v_cache +", "const uint16_t* vrow = k_cache +"),
+    ("cache_value_slot_shifted", "page_size + j % page_size) * n_kv_heads",
+     "page_size + (j + 1) % page_size) * n_kv_heads"),
+    ("cache_sink_dropped", "double den = sinks ? exp(sigma - m) : 0.0;", "double den = 0.0;"),
+    ("cache_rows_without_keys_not_zero", "if (p < 0) return TS_ORACLE_OK;", "if (p < 0) p = 0;"),
 ]
 
 
@@ -55,7 +68,7 @@ def test_pins_catch_mutant(mutant, tmp_path):
     mutated = open(SRC).read()
     for old, new in zip(edits[0::2], edits[1::2]):
         assert old in mutated, f"mutation site for {name} no longer exists in the oracle source"
-        mutated = mutated.replace(old, new)
+        mutated = mutated.replace(old, new, 1)
     path = tmp_path / f"{name}.c"
     path.write_text(mutated)
     lib_path = oracle.build(src=str(path), out=str(tmp_path / f"lib{name}.so"),
