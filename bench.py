@@ -2,6 +2,7 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --sweep            # the chart family: one JSON line per point
+    python bench.py --decode           # decode against a paged KV cache: one line per workload
 
 One step is one ts_mha_prefill call over the whole workload: every stage of the
 operation (tile walk, QK^T, mask, online softmax with sink, PV, epilogue) runs
@@ -14,6 +15,13 @@ only on unmasked pairs.  Printed as one JSON line with a `roofline` object (the
 kernel's average duration from HIP events on the launch stream against the
 bf16 dense MFMA peak) and a `cpu_baseline` object (the fp64 oracle timed on
 this host's cores on a bounded row sample of the same workload).
+
+--decode times ts_mha_decode_with_kvcache on the paged-cache workloads: one step
+is one call (the split kernel and, for long sequences, the merge kernel), and the
+figure is algorithmic HBM bytes per second (every visible cached key and value
+read once, q read, out written).  `value` uses the wall time of eager calls
+(host overhead included); `gpu_avg_us` and `frac_hbm` (against the 8 TB/s roof)
+use the same calls replayed from one captured HIP graph.
 
 Only one GPU is used; --gpus above 1 is refused.
 """
@@ -69,6 +77,15 @@ def algorithmic_bytes(wl) -> int:
     T, D = wl.total_tokens, wl.head_dim
     return T * (2 * wl.n_q_heads * D + 2 * wl.n_kv_heads * D) * 2 + 4 * wl.n_q_heads + \
         4 * (len(wl.seqlens) + 1)
+
+
+def decode_algorithmic_bytes(wl) -> int:
+    """Bytes a decode step must move: visible K and V rows, q, out, seqlens, page ids, sinks."""
+    D = wl.head_dim
+    vis = [min(L, wl.window) if wl.window > 0 else L for L in wl.k_lens]
+    pages = sum(-(-v // wl.page_size) for v in vis)
+    return (sum(vis) * wl.n_kv_heads * D * 2 * 2 + 2 * wl.n_seqs * wl.n_q_heads * D * 2
+            + 4 * wl.n_seqs + 4 * pages + 4 * wl.n_q_heads)
 
 
 def cpu_baseline(wl, inp, target_s: float):
@@ -129,6 +146,8 @@ def main():
                     help="also run a plain 1 GiB device copy (for counter calibration runs)")
     ap.add_argument("--sweep", action="store_true",
                     help="time every chart point (sequence length x batch, full causal) instead")
+    ap.add_argument("--decode", action="store_true",
+                    help="time decode against a paged KV cache on its workloads instead")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {a.gpus} is not supported "
@@ -181,6 +200,70 @@ def main():
         wall = time.perf_counter() - t0
         del q, k, v, sinks, cu, out
         return inp, wall * 1e3 / steps, ev0.elapsed_time(ev1) / steps
+
+    if a.decode:
+        for name, wl in workloads.CACHE_WORKLOADS.items():
+            inp = workloads.make_cache_inputs(wl)
+            q, kc, vc = inp["q"].to(dev), inp["k_cache"].to(dev), inp["v_cache"].to(dev)
+            sinks = inp["sinks"].to(dev) if inp["sinks"] is not None else None
+            lens, table = inp["seqlens_k"].to(dev), inp["block_table"].to(dev)
+            out = torch.empty_like(q)
+            need = tm.ts_mha_decode_workspace_size(wl.n_seqs, wl.n_q_heads, wl.n_kv_heads,
+                                                   wl.head_dim, wl.window, wl.max_seqlen_k)
+            ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+            def dstep():
+                tm.ts_mha_decode_with_kvcache(q, kc, vc, sinks, lens, table, window=wl.window,
+                                              softmax_scale=wl.softmax_scale, out=out,
+                                              max_seqlen_k=wl.max_seqlen_k, workspace=ws,
+                                              stream=stream)
+
+            for _ in range(a.warmup):
+                dstep()
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(a.steps):
+                dstep()
+            torch.cuda.synchronize()
+            ms_step = (time.perf_counter() - t0) * 1e3 / a.steps
+            # GPU time without the host's launch overhead: the same K calls captured
+            # in one HIP graph (the library records no memset), replayed between
+            # one pair of events on the replay stream.
+            graph = torch.cuda.CUDAGraph()
+            gs = torch.cuda.Stream()
+            gs.wait_stream(stream)
+            with torch.cuda.stream(gs):
+                with torch.cuda.graph(graph, stream=gs):
+                    for _ in range(a.steps):
+                        tm.ts_mha_decode_with_kvcache(q, kc, vc, sinks, lens, table,
+                                                      window=wl.window,
+                                                      softmax_scale=wl.softmax_scale, out=out,
+                                                      max_seqlen_k=wl.max_seqlen_k, workspace=ws)
+            # replay() launches on the current stream: the events go on that same stream
+            with torch.cuda.stream(gs):
+                graph.replay()
+                torch.cuda.synchronize()
+                ev0.record(gs)
+                graph.replay()
+                ev1.record(gs)
+            torch.cuda.synchronize()
+            ms_gpu = ev0.elapsed_time(ev1) / a.steps
+            nbytes = decode_algorithmic_bytes(wl)
+            print(json.dumps({"decode_point": name, "batch": wl.n_seqs, "k_len": wl.max_seqlen_k,
+                              "window": wl.window, "page_size": wl.page_size,
+                              "value": round(nbytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s",
+                              "host_us_per_step": round(ms_step * 1e3, 2),
+                              "gpu_avg_us": round(ms_gpu * 1e3, 2),
+                              "algorithmic_bytes": nbytes,
+                              "frac_hbm": round(nbytes / (ms_gpu * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                              "workspace_bytes": need, "steps": a.steps, "warmup": a.warmup}),
+                  flush=True)
+            del graph
+            del q, kc, vc, sinks, lens, table, out, ws
+            torch.cuda.empty_cache()
+        return
 
     if a.sweep:
         for wl in workloads.SWEEP.values():

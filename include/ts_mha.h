@@ -1,9 +1,12 @@
 /*
- * ts_mha.h -- C ABI of the MI355X (gfx950) prefill attention library.
+ * ts_mha.h -- C ABI of the MI355X (gfx950) attention library.
  *
- * One operation: causal grouped-query attention over packed variable-length
- * sequences, with an optional sliding window and an optional per-head
- * attention sink.  This is the `mha_prefill` public call listed in the
+ * The main operation: causal grouped-query attention over packed
+ * variable-length sequences, with an optional sliding window and an optional
+ * per-head attention sink (ts_mha_prefill).  Decode against a paged KV cache
+ * (ts_mha_decode_with_kvcache) applies the same attention to one new query
+ * row per sequence; it is declared further below.  ts_mha_prefill is the
+ * `mha_prefill` public call listed in the
  * TokenSpeed-kernel README, section "Public API" (kept apart there from
  * `mha_prefill_with_kvcache`, so no cache is involved), for the GPT-OSS
  * attention of "TokenSpeed-kernel multi-silicon" (aixai.ru blog), section
@@ -25,9 +28,9 @@
  *
  * General rules for every entry point:
  *  - Every pointer named "device" must point to device memory of the current
- *    HIP device; the caller owns all buffers and keeps them alive until the
- *    work on `stream` has finished.  The library allocates no device memory
- *    and keeps no per-call state.
+ *    HIP device; the caller owns all buffers (a decode workspace included) and
+ *    keeps them alive until the work on `stream` has finished.  The library
+ *    allocates no device memory and keeps no per-call state.
  *  - Arguments are validated on the host before any HIP call; a rejected call
  *    launches nothing and returns a negative TS_MHA_ERR_* code.  No C++
  *    exception crosses this interface.
@@ -58,7 +61,11 @@ extern "C" {
 #define TS_MHA_ERR_ARCH (-7)         /* the current device is not gfx950 */
 #define TS_MHA_ERR_LAUNCH (-8)       /* the HIP launch failed; ts_mha_strerror adds the HIP error text */
 #define TS_MHA_ERR_SEQLENS (-9)      /* only with TS_MHA_VALIDATE=1 in the environment: cu_seqlens[0] != 0,
-                                        cu_seqlens decreasing, or a length above max_seqlen */
+                                        cu_seqlens decreasing, or a length above max_seqlen; for the
+                                        cache call a seqlens_k entry outside [0, max_seqlen_k] */
+#define TS_MHA_ERR_WORKSPACE (-10)   /* decode: workspace NULL or smaller than ts_mha_decode_workspace_size */
+#define TS_MHA_ERR_PAGES (-11)       /* only with TS_MHA_VALIDATE=1: a block-table entry that a sequence
+                                        needs is outside [0, n_pages) */
 
 /*
  * ts_mha_prefill -- enqueue one prefill attention pass (the operation above).
@@ -105,6 +112,74 @@ const char* ts_mha_strerror(int code);
  *  length is negative.
  */
 int64_t ts_mha_unmasked_pairs(const int32_t* cu_seqlens_host, int32_t n_seqs, int32_t window);
+
+/*
+ * ts_mha_decode_with_kvcache -- decode attention against a paged KV cache:
+ * one new query row per sequence, every query head.  The TokenSpeed-kernel
+ * README, section "Public API", lists `mha_decode_with_kvcache` beside
+ * `mha_prefill`, and "TokenSpeed-kernel multi-silicon" (aixai.ru blog),
+ * section "Архитектура: три слоя вместо лабиринта", names it as one of the
+ * runtime's attention calls; the pages give no signature or layout.  Readings
+ * taken here:
+ *  - the cache already holds the new token's own key and value (the caller
+ *    writes them first); seqlens_k[b] counts every cached key of sequence b,
+ *    that one included, so the query sits at position p = seqlens_k[b] - 1;
+ *  - key position j of sequence b lives in page block_table[b][j / page_size],
+ *    slot j % page_size, of k_cache / v_cache [n_pages][page_size][n_kv_heads][64];
+ *  - visible keys, sink, scale and the query-head to KV-head mapping are those
+ *    of ts_mha_prefill at position p: keys j <= p with p - j < window when
+ *    window > 0;
+ *  - a sequence with seqlens_k[b] == 0 has no key and its output rows are zero.
+ *
+ *  q             device, bf16 [n_seqs][n_q_heads][64], 16-byte aligned
+ *  k_cache, v_cache  device, bf16 [n_pages][page_size][n_kv_heads][64], 16-byte
+ *                aligned.  Slots no sequence uses (and slots at or past
+ *                seqlens_k[b] in a sequence's last page) may hold anything,
+ *                NaN included: they are never read.
+ *  sinks         device, fp32 [n_q_heads], or NULL for no sink
+ *  seqlens_k     device, int32 [n_seqs], each in [0, max_seqlen_k]
+ *  block_table   device, int32 [n_seqs][pages_per_seq]; the first
+ *                ceil(seqlens_k[b] / page_size) entries of row b are page ids in
+ *                [0, n_pages); the rest are ignored
+ *  n_q_heads, n_kv_heads, head_dim, window, softmax_scale   as for ts_mha_prefill
+ *  out           device, bf16 [n_seqs][n_q_heads][64], 16-byte aligned, fully
+ *                overwritten; must not overlap any input
+ *  n_seqs        >= 0; 0 is a no-op
+ *  n_pages       > 0, pages in the pool
+ *  page_size     keys per page: a power of two >= 16
+ *  pages_per_seq > 0, the row length of block_table
+ *  max_seqlen_k  >= every seqlens_k[b], <= pages_per_seq * page_size and <= 2^30;
+ *                sizes the launch (keys past it are not read)
+ *  workspace     device scratch for partial results of long sequences, 256-byte
+ *                aligned, at least ts_mha_decode_workspace_size(...) bytes (NULL
+ *                allowed when that is 0); caller-owned, contents need no
+ *                initialisation and are meaningless afterwards; calls that
+ *                share a workspace must not run concurrently
+ *  workspace_bytes  its size in bytes
+ *  stream        hipStream_t to enqueue on; NULL = the default stream
+ *
+ *  Out-of-contract seqlens_k or block_table values never make the kernels
+ *  read outside the block table or the cache pool (page ids are clamped into
+ *  the pool), but the results are then meaningless; TS_MHA_VALIDATE=1 checks
+ *  them on the host first (a synchronising read-back).
+ *  Returns TS_MHA_OK or a TS_MHA_ERR_* code.
+ */
+int ts_mha_decode_with_kvcache(const void* q, const void* k_cache, const void* v_cache,
+                               const float* sinks, const int32_t* seqlens_k,
+                               const int32_t* block_table, int32_t n_q_heads, int32_t n_kv_heads,
+                               int32_t head_dim, int32_t window, float softmax_scale, void* out,
+                               int32_t n_seqs, int32_t n_pages, int32_t page_size,
+                               int32_t pages_per_seq, int32_t max_seqlen_k, void* workspace,
+                               int64_t workspace_bytes, void* stream);
+
+/*
+ * ts_mha_decode_workspace_size -- bytes of workspace a ts_mha_decode_with_kvcache
+ * call with these arguments needs (0: none).  The split of long sequences into
+ * key chunks depends only on these arguments.  Returns a negative TS_MHA_ERR_*
+ * code for shapes the decode call would reject.
+ */
+int64_t ts_mha_decode_workspace_size(int32_t n_seqs, int32_t n_q_heads, int32_t n_kv_heads,
+                                     int32_t head_dim, int32_t window, int32_t max_seqlen_k);
 
 #ifdef __cplusplus
 }

@@ -20,6 +20,7 @@ ERROR_NAMES = {
     -1: "TS_MHA_ERR_NULL_ARG", -2: "TS_MHA_ERR_BAD_SHAPE", -3: "TS_MHA_ERR_UNSUPPORTED",
     -4: "TS_MHA_ERR_BAD_SCALE", -5: "TS_MHA_ERR_ALIGN", -6: "TS_MHA_ERR_NO_DEVICE",
     -7: "TS_MHA_ERR_ARCH", -8: "TS_MHA_ERR_LAUNCH", -9: "TS_MHA_ERR_SEQLENS",
+    -10: "TS_MHA_ERR_WORKSPACE", -11: "TS_MHA_ERR_PAGES",
 }
 
 _lib = None
@@ -47,6 +48,12 @@ def lib() -> ctypes.CDLL:
         L.ts_mha_strerror.restype = ctypes.c_char_p
         L.ts_mha_unmasked_pairs.argtypes = [ctypes.POINTER(ctypes.c_int32), i32, i32]
         L.ts_mha_unmasked_pairs.restype = i64
+        L.ts_mha_decode_with_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                                 ctypes.c_float, vp, i32, i32, i32, i32, i32, vp,
+                                                 i64, vp]
+        L.ts_mha_decode_with_kvcache.restype = ctypes.c_int
+        L.ts_mha_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+        L.ts_mha_decode_workspace_size.restype = i64
         _lib = L
     return _lib
 
@@ -132,5 +139,96 @@ def ts_mha_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks, cu_
     return out
 
 
-# The operation's name in the public API the pages list.
+def _check_tensor(name, t, dtype, dim, dev):
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or t.dim() != dim:
+        raise TypeError(f"{name} must be a {dim}-D {dtype} tensor")
+    if t.device != dev or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor on {dev}")
+
+
+def _stream_handle(stream, dev):
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def ts_mha_decode_workspace_size(n_seqs: int, n_q_heads: int, n_kv_heads: int, head_dim: int = 64,
+                                 window: int = 0, max_seqlen_k: int = 0) -> int:
+    """Workspace bytes a decode call with these arguments needs (0: none)."""
+    r = lib().ts_mha_decode_workspace_size(int(n_seqs), int(n_q_heads), int(n_kv_heads),
+                                           int(head_dim), int(window), int(max_seqlen_k))
+    if r < 0:
+        raise TsMhaError(int(r), ts_mha_strerror(int(r)))
+    return int(r)
+
+
+def ts_mha_decode_with_kvcache(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                               sinks, seqlens_k: torch.Tensor, block_table: torch.Tensor,
+                               window: int = 0, softmax_scale: float | None = None, out=None,
+                               max_seqlen_k: int | None = None, workspace=None,
+                               stream=None) -> torch.Tensor:
+    """Decode attention of one new query row per sequence against a paged KV cache.
+
+    q [B, Hq, 64] bf16; k_cache / v_cache [n_pages, page_size, Hkv, 64] bf16;
+    seqlens_k int32 [B] (cached keys, the new token's own included); block_table
+    int32 [B, pages_per_seq]; sinks fp32 [Hq] or None.  max_seqlen_k sizes the
+    launch; if omitted it is read back from seqlens_k (synchronising).  The
+    workspace for long sequences is taken from `workspace` (a uint8 tensor) or
+    allocated here.  Runs on `stream` (default: torch's current stream).
+    """
+    dev = q.device
+    _check_tensor("q", q, torch.bfloat16, 3, dev)
+    _check_tensor("k_cache", k_cache, torch.bfloat16, 4, dev)
+    _check_tensor("v_cache", v_cache, torch.bfloat16, 4, dev)
+    _check_tensor("seqlens_k", seqlens_k, torch.int32, 1, dev)
+    _check_tensor("block_table", block_table, torch.int32, 2, dev)
+    if not q.is_cuda:
+        raise ValueError("q must be a GPU tensor")
+    B, hq, D = q.shape
+    n_pages, page_size, hkv, Dk = k_cache.shape
+    if v_cache.shape != k_cache.shape or Dk != D:
+        raise ValueError("k_cache and v_cache must both be [n_pages, page_size, Hkv, D]")
+    if seqlens_k.shape != (B,) or block_table.shape[0] != B:
+        raise ValueError("seqlens_k must be [B] and block_table [B, pages_per_seq]")
+    if sinks is not None:
+        _check_tensor("sinks", sinks, torch.float32, 1, dev)
+        if sinks.shape != (hq,):
+            raise ValueError("sinks must be [Hq]")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor("out", out, torch.bfloat16, 3, dev)
+        if out.shape != q.shape:
+            raise ValueError("out must be shaped like q")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seqlens_k", seqlens_k),
+                    ("block_table", block_table)) + ((("sinks", sinks),) if sinks is not None else ()):
+        if _overlaps(out, t):
+            raise ValueError(f"out must not overlap {name}")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / (D ** 0.5)
+    if B == 0:
+        return out
+    if max_seqlen_k is None:
+        max_seqlen_k = int(seqlens_k.max().cpu())
+    need = ts_mha_decode_workspace_size(B, hq, hkv, D, window, max_seqlen_k)
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        elif not isinstance(workspace, torch.Tensor) or workspace.device != dev \
+                or workspace.numel() * workspace.element_size() < need or not workspace.is_contiguous():
+            raise ValueError(f"workspace must be a contiguous tensor of at least {need} bytes on {dev}")
+    ws_ptr = workspace.data_ptr() if (workspace is not None and need > 0) else None
+    ws_bytes = workspace.numel() * workspace.element_size() if ws_ptr else 0
+    rc = lib().ts_mha_decode_with_kvcache(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        None if sinks is None else sinks.data_ptr(), seqlens_k.data_ptr(), block_table.data_ptr(),
+        hq, hkv, D, int(window), float(softmax_scale), out.data_ptr(), B, n_pages, page_size,
+        block_table.shape[1], int(max_seqlen_k), ws_ptr, ws_bytes, _stream_handle(stream, dev))
+    if rc != TS_MHA_OK:
+        raise TsMhaError(rc, ts_mha_strerror(rc))
+    return out
+
+
+# The operations' names in the public API the pages list.
 mha_prefill = ts_mha_prefill
+mha_decode_with_kvcache = ts_mha_decode_with_kvcache

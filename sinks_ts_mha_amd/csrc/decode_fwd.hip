@@ -1,0 +1,473 @@
+// decode_fwd.hip -- gfx950 kernels of decode attention against a paged KV
+// cache: one new query row per sequence (all query heads) attends to the
+// sequence's cached keys, with the GPT-OSS attention of "TokenSpeed-kernel
+// multi-silicon" (aixai.ru blog), section "Числа: Gluon на AMD MI355X":
+// grouped query heads, an optional sliding window and an optional per-head
+// sink.  This is the `mha_decode_with_kvcache` call of the TokenSpeed-kernel
+// README, section "Public API"; the pages give it no signature, and the
+// readings taken are stated in include/ts_mha.h.
+//
+// Decode reads every cached key and value once and does 2 x 64 flops per key
+// and query head, so it is bound by HBM bandwidth, not by the matrix cores.
+// The design is about keeping enough bytes in flight:
+//
+// Work decomposition.  One work-group per (sequence, KV head, key chunk); the
+// host picks the chunk length (a multiple of 128 keys, at most 8192) so that
+// the grid fills every CU once (a work-group takes most of a CU's LDS), and
+// does not split a sequence when there are enough (sequence, KV head) pairs.  Its four waves take the chunk's
+// 32-key tiles round robin; each wave streams its tiles through a private
+// ring of four LDS stages with wave-wide buffer-to-LDS loads, three tiles
+// ahead, so the walk needs no barrier.
+//
+// Paging.  A 32-key tile is loaded as four groups of 8 keys; with pages of at
+// least 16 keys a group never straddles a page, so each load takes one page
+// id (from a copy of the chunk's block-table slice in LDS) and addresses that
+// page through its own buffer descriptor.  Keys at or past the sequence end
+// fall outside the descriptor's range and read as zeros, so cache slots that
+// were never written cannot leak into the result.
+//
+// Arithmetic.  The G query heads of the KV head are the 16 columns of
+// 16 x 16 x 32 bf16 MFMAs (G <= 16; the other columns are zero): S^T = K Q^T
+// per 16 keys, then O^T += V^T P^T per 32 keys with V^T read by
+// ds_read_b64_tr_b16.  Each lane holds one query (lane % 16), so the running
+// maximum, the rescale of O and the probabilities need no lane exchange
+// except the tile maximum over the four lane groups.  Softmax in base 2:
+// t = s * scale * log2(e).
+//
+// Merge.  The four waves combine their (m, l, O) through LDS.  With one chunk
+// per sequence the work-group adds the sink's term exp2(sigma - m), normalises
+// and stores bf16; otherwise it stores the chunk's (m, l, O) in fp32 and
+// decode_merge combines the chunks of each sequence and adds the sink.
+#include "decode_fwd.h"
+
+#include <math.h>
+
+#include <algorithm>
+
+#include "cdna4.h"
+
+namespace tsmha {
+
+namespace {
+
+using namespace cdna4;
+
+constexpr int kD = 64;                            // head_dim
+constexpr int kRowBytes = kD * 2;                 // one K or V row in bytes
+constexpr int kTileKeys = 32;                     // keys per LDS tile
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStages = 4;                        // LDS tiles per wave, three in flight
+constexpr int kTileBytes = kTileKeys * kRowBytes;  // one tile of K (or V): 4 KiB
+constexpr int kLoads = kTileBytes / 1024;         // wave-wide loads per tile and operand
+constexpr int kChunkMax = 8192;                   // keys per work-group at most
+constexpr int kMinPage = 16;
+constexpr int kPageSlots = kChunkMax / kMinPage + 2;
+constexpr int kTargetGroups = 256;                // one work-group per CU
+
+struct DParams {
+  const uint16_t* q;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  const float* sinks;
+  const int32_t* seqlens_k;
+  const int32_t* block_table;
+  uint16_t* out;
+  float* ws_ml;          // [n_splits][n_seqs][Hq][2]: (m, l) of each chunk
+  float* ws_o;           // [n_splits][n_seqs][Hq][64]: unnormalised O of each chunk
+  int64_t page_elems;    // bf16 elements per page: page_size * n_kv_heads * 64
+  int32_t page_bytes;
+  int32_t n_kv_heads;
+  int32_t n_seqs;
+  int32_t n_pages;
+  int32_t page_shift;
+  int32_t pages_per_seq;
+  int32_t window;
+  int32_t chunk;
+  int32_t n_splits;
+  float c;               // softmax_scale * log2(e)
+};
+
+// First key of a sequence's first chunk: the first visible key (window), rounded
+// down to a tile boundary.
+__device__ __forceinline__ int first_tile_key(int L, int window) {
+  const int lo = window > 0 ? max(0, L - window) : 0;
+  return lo & ~(kTileKeys - 1);
+}
+
+__device__ __forceinline__ float lane_group_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+__device__ __forceinline__ float lane_group_sum(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+
+}  // namespace
+
+template <int G>
+__global__ void __launch_bounds__(kThreads, 1) decode_split_d64(DParams p) {
+  static_assert(G >= 1 && G <= 16, "the query heads of a KV head fill at most 16 MFMA columns");
+  __shared__ u32x4 ring[kWaves * kStages * 2 * kTileBytes / 16];  // [wave][stage][K, V][tile]
+  __shared__ float mo[kWaves][G][kD];                             // each wave's O
+  __shared__ float ml[kWaves][G][2];                              // each wave's (m, l)
+  __shared__ int pages[kPageSlots];                               // the chunk's page ids
+
+  const int Hkv = p.n_kv_heads;
+  const int Hq = Hkv * G;
+  const int id = blockIdx.x;
+  const int g = id % Hkv;
+  const int rest = id / Hkv;
+  const int b = rest % p.n_seqs;
+  const int split = rest / p.n_seqs;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int r16 = lane & 15;  // this lane's query (head g * G + r16 when r16 < G)
+  const int grp = lane >> 4;
+
+  const int L = p.seqlens_k[b];
+  const int lo = p.window > 0 ? max(0, L - p.window) : 0;
+  const int start = first_tile_key(L, p.window) + split * p.chunk;
+  const int end = min(L, start + p.chunk);
+  if (start >= end) {
+    // No key in this chunk.  With one chunk per sequence the rows are written
+    // here (a sequence without keys has zero output); otherwise decode_merge
+    // skips the chunk.
+    if (p.n_splits == 1 && tid < G * 8)
+      *(u32x4*)(p.out + ((int64_t)b * Hq + g * G) * kD + tid * 8) = u32x4{0u, 0u, 0u, 0u};
+    return;
+  }
+
+  // ---- the chunk's page ids into LDS (clamped into the table and the pool, so
+  // a malformed table cannot move a load outside the cache), and this lane's
+  // query fragments: lane l holds head_dim elements 32 ks + 8 grp .. + 7 of
+  // query r16, the B operand of S^T = K Q^T.
+  const int pidx0 = start >> p.page_shift;
+  const int npg = min(((end - 1) >> p.page_shift) - pidx0 + 1, kPageSlots);
+  {
+    const int32_t* brow = p.block_table + (int64_t)b * p.pages_per_seq;
+    for (int i = tid; i < npg; i += kThreads) {
+      const int pg = brow[min(pidx0 + i, p.pages_per_seq - 1)];
+      pages[i] = min(max(pg, 0), p.n_pages - 1);
+    }
+  }
+  bf16x8 qf[2];
+  if (r16 < G) {
+    const uint16_t* qrow = p.q + ((int64_t)b * Hq + g * G + r16) * kD;
+    qf[0] = *(const bf16x8*)(qrow + 8 * grp);
+    qf[1] = *(const bf16x8*)(qrow + 32 + 8 * grp);
+  } else {
+    qf[0] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    qf[1] = qf[0];
+  }
+  float sink_t = -INFINITY;
+  if (p.sinks && r16 < G) sink_t = p.sinks[g * G + r16] * kLog2e;
+  __syncthreads();  // page ids visible to every wave
+  // The query loads complete here, before the tile loads below go out, so the
+  // compiler's own waits never count those.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  // ---- tile loads.  The wave's i-th tile is the work-group's tile w + 4 i and
+  // goes to stage i % kStages.  Load `it` brings keys 8 it .. 8 it + 7 of the
+  // tile: lane l fetches 16 bytes of key 8 it + l / 8, placed at its swizzled
+  // chunk.  Loads past the wave's last tile still go out, with every lane out
+  // of range, so the number in flight is the same on every iteration.
+  const int nt = (end - start + kTileKeys - 1) / kTileKeys;
+  const int my_tiles = nt > w ? (nt - w + kWaves - 1) / kWaves : 0;
+  const int pmask = (1 << p.page_shift) - 1;
+  int dch[kLoads];
+#pragma unroll
+  for (int it = 0; it < kLoads; ++it) {
+    const int row = 8 * it + (lane >> 3);
+    dch[it] = ((lane & 7) ^ swz_key(row)) * 16 + g * kRowBytes;
+  }
+  const uint32_t ring_w = lds_addr(ring) + w * kStages * 2 * kTileBytes;
+  auto issue = [&](int i) {
+    const int t = w + kWaves * i;
+    const bool live = i < my_tiles;
+    const int tile_key = start + kTileKeys * t;
+    const uint32_t dk = ring_w + (i % kStages) * 2 * kTileBytes;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int key0 = tile_key + 16 * half;
+      const int slot = min(max((key0 >> p.page_shift) - pidx0, 0), npg - 1);
+      const int pg = live ? __builtin_amdgcn_readfirstlane(pages[slot]) : 0;
+      const int64_t off = (int64_t)pg * p.page_elems;
+      const i32x4 rk = buffer_rsrc(p.kc + off, p.page_bytes);
+      const i32x4 rv = buffer_rsrc(p.vc + off, p.page_bytes);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int it = 2 * half + j;
+        const int key = tile_key + 8 * it + (lane >> 3);
+        const int vo = (live && key < end) ? (key & pmask) * Hkv * kRowBytes + dch[it] : p.page_bytes;
+        lds_dma16(dk + it * 1024, rk, vo);
+        lds_dma16(dk + kTileBytes + it * 1024, rv, vo);
+      }
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < kStages - 1; ++i) issue(i);
+
+  // Per-lane byte offsets of the V^T reads within a tile: the lanes of group
+  // grp read keys 4 grp + r16 / 4 (low half) and 16 more (high half), head_dim
+  // columns 16 db + 4 (r16 % 4) .. + 3; the transpose hands lane r16 column
+  // 16 db + r16 of those four keys.  Rows 16 apart share their swizzle key.
+  uint32_t voff[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int row = 4 * grp + (r16 >> 2);
+    const int d = 16 * db + 4 * (r16 & 3);
+    voff[db] = row * kRowBytes + (((d >> 3) ^ swz_key(row)) << 4) + (d & 7) * 2;
+  }
+
+  float m = -INFINITY;  // running maximum of t for query r16 (identical across lane groups)
+  float lsum = 0.f;     // this lane's share of the row sum
+  f32x4 o[4];           // O^T: element e of block db is head_dim 16 db + 4 grp + e, query r16
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int i = 0; i < my_tiles; ++i) {
+    issue(i + kStages - 1);
+    wait_vmem<(kStages - 1) * 2 * kLoads>();  // tile i has landed
+    const lds_char* kt = (const lds_char*)ring + (w * kStages + i % kStages) * 2 * kTileBytes;
+    const lds_char* vt = kt + kTileBytes;
+    const int tile_key = start + kTileKeys * (w + kWaves * i);
+    const bool edge = tile_key < lo || tile_key + kTileKeys > L;
+
+    // S^T for keys 16 kb .. 16 kb + 15: element e is key 16 kb + 4 grp + e.
+    // Keys outside [lo, L) start from -inf, so the MFMA applies the mask.
+    f32x4 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (edge) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = tile_key + 16 * kb + 4 * grp + e;
+          acc[e] = (key >= lo && key < L) ? 0.f : -INFINITY;
+        }
+      }
+      const bf16x8 k0 = *(const bf16x8*)(kt + swz(16 * kb + r16, grp) * 16);
+      const bf16x8 k1 = *(const bf16x8*)(kt + swz(16 * kb + r16, 4 + grp) * 16);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[0], acc, 0, 0, 0);
+      s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[1], acc, 0, 0, 0);
+    }
+
+    // Streaming softmax of query r16 over the tile's 32 keys.
+    float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    const float mn = fmaxf(m, lane_group_max(mt) * p.c);
+    const float mu = (mn == -INFINITY) ? 0.f : mn;
+    const float alpha = __builtin_amdgcn_exp2f(m - mu);
+    m = mn;
+    bf16x8 pf;  // P^T, the B operand of the PV MFMA: keys 4 grp + e, then 16 + 4 grp + e
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(fmaf(s[kb][e], p.c, -mu));
+        pf[4 * kb + e] = (__bf16)pe;
+        ps += pe;
+      }
+    lsum = fmaf(lsum, alpha, ps);
+
+    // O^T = alpha O^T + V^T P^T, the A operand's keys in P^T's order.
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + voff[db]));
+      const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + voff[db] + 16 * kRowBytes));
+      const u32x2 u0 = __builtin_bit_cast(u32x2, t0);
+      const u32x2 u1 = __builtin_bit_cast(u32x2, t1);
+      const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{u0[0], u0[1], u1[0], u1[1]});
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf, o[db] * alpha, 0, 0, 0);
+    }
+  }
+  // The loads past the last tile land before the wave may leave its LDS.
+  wait_vmem<0>();
+
+  // ---- combine the four waves.
+  lsum = lane_group_sum(lsum);
+  if (r16 < G) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mo[w][r16][16 * db + 4 * grp + e] = o[db][e];
+    if (grp == 0) {
+      ml[w][r16][0] = m;
+      ml[w][r16][1] = lsum;
+    }
+  }
+  __syncthreads();
+  if (tid < G * 16) {
+    const int q = tid >> 4;
+    const int d0 = 4 * (tid & 15);
+    const int h = g * G + q;
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, ml[v][q][0]);
+    float lt = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+      const float f = __builtin_amdgcn_exp2f(ml[v][q][0] - M);  // 0 for a wave without tiles
+      lt = fmaf(f, ml[v][q][1], lt);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(f, mo[v][q][d0 + e], acc[e]);
+    }
+    if (p.n_splits == 1) {
+      const float st = __shfl(sink_t, q);  // lane q holds the sink of query q (wave 0)
+      float den = lt;
+      float scale = 1.f;
+      if (p.sinks) {
+        const float M2 = fmaxf(M, st);
+        scale = __builtin_amdgcn_exp2f(M - M2);
+        den = fmaf(lt, scale, __builtin_amdgcn_exp2f(st - M2));
+      }
+      const float inv = scale / den;
+      bf16x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = (__bf16)(acc[e] * inv);
+      *(bf16x4*)(p.out + ((int64_t)b * Hq + h) * kD + d0) = r;
+    } else {
+      const int64_t row = ((int64_t)split * p.n_seqs + b) * Hq + h;
+      *(f32x4*)(p.ws_o + row * kD + d0) = acc;
+      if (d0 == 0) {
+        p.ws_ml[2 * row] = M;
+        p.ws_ml[2 * row + 1] = lt;
+      }
+    }
+  }
+}
+
+// Combine the chunks of each (sequence, query head).  One work-group per
+// (sequence, query head): thread (sl, dc) folds chunks sl, sl + 16, ... of
+// head_dim elements 4 dc .. 4 dc + 3 into a running (m, l, O), the 16 chunk
+// lanes then combine by a butterfly, and the sink's term joins the
+// denominator.  The chunk loads of one thread are independent, so the loop
+// keeps several in flight.
+constexpr int kMergeLanes = 16;
+
+__device__ __forceinline__ void fold(float& m, float& l, f32x4& o, float m2, float l2, const f32x4& o2) {
+  const float mn = fmaxf(m, m2);
+  const float mu = (mn == -INFINITY) ? 0.f : mn;
+  const float a = __builtin_amdgcn_exp2f(m - mu);
+  const float b = __builtin_amdgcn_exp2f(m2 - mu);
+  l = fmaf(l, a, l2 * b);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = fmaf(o[e], a, o2[e] * b);
+  m = mn;
+}
+
+__global__ void __launch_bounds__(256) decode_merge_d64(DParams p, int G) {
+  const int Hq = p.n_kv_heads * G;
+  const int h = blockIdx.x % Hq;
+  const int b = blockIdx.x / Hq;
+  const int tid = threadIdx.x;
+  const int sl = tid & (kMergeLanes - 1);
+  const int dc = tid >> 4;
+  const int L = p.seqlens_k[b];
+  const int n_valid = L > 0 ? min(p.n_splits, (L - first_tile_key(L, p.window) + p.chunk - 1) / p.chunk) : 0;
+  float m = -INFINITY, l = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int s = sl; s < n_valid; s += kMergeLanes) {
+    const int64_t row = ((int64_t)s * p.n_seqs + b) * Hq + h;
+    fold(m, l, o, p.ws_ml[2 * row], p.ws_ml[2 * row + 1], *(const f32x4*)(p.ws_o + row * kD + 4 * dc));
+  }
+#pragma unroll
+  for (int x = 1; x < kMergeLanes; x <<= 1) {
+    f32x4 o2;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o2[e] = __shfl_xor(o[e], x);
+    fold(m, l, o, __shfl_xor(m, x), __shfl_xor(l, x), o2);
+  }
+  if (sl != 0) return;
+  // the sink's term, then normalise; no key and no sink leaves a zero row
+  const float st = p.sinks ? p.sinks[h] * kLog2e : -INFINITY;
+  fold(m, l, o, st, 1.f, f32x4{0.f, 0.f, 0.f, 0.f});
+  const float inv = (l > 0.f) ? 1.f / l : 0.f;
+  bf16x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = (__bf16)(o[e] * inv);
+  *(bf16x4*)(p.out + ((int64_t)b * Hq + h) * kD + 4 * dc) = r;
+}
+
+namespace {
+
+template <int G>
+hipError_t launch_group(const DParams& kp, int64_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_split_d64<G>), dim3((unsigned)grid), dim3(kThreads), 0, stream, kp);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || kp.n_splits == 1) return err;
+  hipLaunchKernelGGL(decode_merge_d64, dim3((unsigned)(kp.n_seqs * kp.n_kv_heads * G)), dim3(256), 0,
+                     stream, kp, G);
+  return hipGetLastError();
+}
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+DecodePlan decode_plan(const DecodeArgs& a) {
+  DecodePlan pl{0, -1, 0};
+  int64_t span = a.max_seqlen_k;
+  if (a.window > 0) span = std::min<int64_t>(span, (int64_t)a.window + kTileKeys - 1);
+  const int64_t tiles = std::max<int64_t>(1, (span + kTileKeys - 1) / kTileKeys);
+  const int64_t base = std::max<int64_t>(1, (int64_t)a.n_seqs * a.n_kv_heads);
+  const int64_t want = std::max<int64_t>(1, (kTargetGroups + base - 1) / base);
+  int64_t ct = (tiles + want - 1) / want;
+  ct = std::min<int64_t>(std::max<int64_t>(4, (ct + 3) / 4 * 4), kChunkMax / kTileKeys);
+  const int64_t n_splits = (tiles + ct - 1) / ct;
+  if (n_splits * base > 0x7fffffffLL) return pl;
+  pl.chunk = (int32_t)(ct * kTileKeys);
+  pl.n_splits = (int32_t)n_splits;
+  if (n_splits > 1) {
+    const int64_t rows = n_splits * a.n_seqs * (int64_t)a.n_q_heads;
+    pl.workspace_bytes = align_up(rows * 2 * 4, 256) + rows * kD * 4;
+  }
+  return pl;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, void* workspace,
+                         hipStream_t stream) {
+  const int G = a.n_q_heads / a.n_kv_heads;
+  DParams kp;
+  kp.q = static_cast<const uint16_t*>(a.q);
+  kp.kc = static_cast<const uint16_t*>(a.k_cache);
+  kp.vc = static_cast<const uint16_t*>(a.v_cache);
+  kp.sinks = a.sinks;
+  kp.seqlens_k = a.seqlens_k;
+  kp.block_table = a.block_table;
+  kp.out = static_cast<uint16_t*>(a.out);
+  const int64_t rows = (int64_t)plan.n_splits * a.n_seqs * a.n_q_heads;
+  kp.ws_ml = plan.n_splits > 1 ? static_cast<float*>(workspace) : nullptr;
+  kp.ws_o = plan.n_splits > 1
+                ? reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(rows * 2 * 4, 256))
+                : nullptr;
+  kp.page_elems = (int64_t)a.page_size * a.n_kv_heads * kD;
+  kp.page_bytes = a.page_size * a.n_kv_heads * kRowBytes;
+  kp.n_kv_heads = a.n_kv_heads;
+  kp.n_seqs = a.n_seqs;
+  kp.n_pages = a.n_pages;
+  kp.page_shift = __builtin_ctz((unsigned)a.page_size);
+  kp.pages_per_seq = a.pages_per_seq;
+  kp.window = a.window;
+  kp.chunk = plan.chunk;
+  kp.n_splits = plan.n_splits;
+  kp.c = a.softmax_scale * kLog2e;
+  const int64_t grid = (int64_t)a.n_seqs * a.n_kv_heads * plan.n_splits;
+  switch (G) {
+    case 1: return launch_group<1>(kp, grid, stream);
+    case 2: return launch_group<2>(kp, grid, stream);
+    case 4: return launch_group<4>(kp, grid, stream);
+    case 8: return launch_group<8>(kp, grid, stream);
+    case 16: return launch_group<16>(kp, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace tsmha

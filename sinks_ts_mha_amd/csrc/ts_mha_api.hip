@@ -1,7 +1,7 @@
 // ts_mha_api.hip -- the C ABI declared in include/ts_mha.h: host-side argument
 // validation, device capability check, error text, and the pair count used by
-// the throughput metric.  All arithmetic of the operation runs in the kernels
-// of prefill_fwd.hip.
+// the throughput metric.  All arithmetic of the operations runs in the kernels
+// of prefill_fwd.hip and decode_fwd.hip.
 #include "ts_mha.h"
 
 #include <hip/hip_runtime.h>
@@ -14,6 +14,7 @@
 #include <mutex>
 #include <vector>
 
+#include "decode_fwd.h"
 #include "prefill_fwd.h"
 
 namespace {
@@ -71,6 +72,62 @@ int validate_seqlens(const int32_t* cu, int32_t n_seqs, int32_t max_seqlen, hipS
   return TS_MHA_OK;
 }
 
+// Debug mode for the cache calls: read seqlens_k and the block table back and
+// check them against the documented contract.
+int validate_cache(const int32_t* seqlens_k, const int32_t* block_table, int32_t n_seqs,
+                   int32_t n_pages, int32_t page_size, int32_t pages_per_seq, int32_t max_seqlen_k,
+                   hipStream_t stream) {
+  std::vector<int32_t> lens((size_t)n_seqs);
+  std::vector<int32_t> table((size_t)n_seqs * pages_per_seq);
+  if (hipMemcpyAsync(lens.data(), seqlens_k, sizeof(int32_t) * lens.size(), hipMemcpyDeviceToHost,
+                     stream) != hipSuccess ||
+      hipMemcpyAsync(table.data(), block_table, sizeof(int32_t) * table.size(), hipMemcpyDeviceToHost,
+                     stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess) {
+    snprintf(g_launch_msg, sizeof g_launch_msg, "%s", hipGetErrorString(hipGetLastError()));
+    return TS_MHA_ERR_LAUNCH;
+  }
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    if (lens[b] < 0 || lens[b] > max_seqlen_k) return TS_MHA_ERR_SEQLENS;
+    const int64_t need = ((int64_t)lens[b] + page_size - 1) / page_size;
+    for (int64_t i = 0; i < need; ++i) {
+      const int32_t pg = table[(size_t)b * pages_per_seq + i];
+      if (pg < 0 || pg >= n_pages) return TS_MHA_ERR_PAGES;
+    }
+  }
+  return TS_MHA_OK;
+}
+
+bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// Checks shared by the cache calls; TS_MHA_OK when the shapes are acceptable.
+int check_cache_shapes(int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float softmax_scale,
+                       int32_t n_seqs, int32_t n_pages, int32_t page_size, int32_t pages_per_seq,
+                       int32_t max_seqlen_k) {
+  if (n_q_heads <= 0 || n_kv_heads <= 0 || n_seqs < 0 || max_seqlen_k < 0) return TS_MHA_ERR_BAD_SHAPE;
+  if (n_q_heads % n_kv_heads != 0) return TS_MHA_ERR_BAD_SHAPE;
+  if (n_pages <= 0 || pages_per_seq <= 0 || !is_pow2(page_size) || page_size < 16) return TS_MHA_ERR_BAD_SHAPE;
+  if ((int64_t)page_size * n_kv_heads * head_dim * 2 > 0x7fff0000LL) return TS_MHA_ERR_BAD_SHAPE;
+  if (max_seqlen_k > (1 << 30) || (int64_t)max_seqlen_k > (int64_t)pages_per_seq * page_size)
+    return TS_MHA_ERR_BAD_SHAPE;
+  const int32_t G = n_q_heads / n_kv_heads;
+  if (head_dim != 64) return TS_MHA_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return TS_MHA_ERR_UNSUPPORTED;
+  if (!isfinite(softmax_scale) || !(softmax_scale > 0.f)) return TS_MHA_ERR_BAD_SCALE;
+  return TS_MHA_OK;
+}
+
+tsmha::DecodeArgs decode_args(int32_t n_q_heads, int32_t n_kv_heads, int32_t window, int32_t n_seqs,
+                              int32_t max_seqlen_k) {
+  tsmha::DecodeArgs a{};
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.window = window;
+  a.n_seqs = n_seqs;
+  a.max_seqlen_k = max_seqlen_k;
+  return a;
+}
+
 }  // namespace
 
 extern "C" int ts_mha_prefill(const void* q, const void* k, const void* v, const float* sinks,
@@ -123,19 +180,80 @@ extern "C" int ts_mha_prefill(const void* q, const void* k, const void* v, const
   return TS_MHA_OK;
 }
 
+extern "C" int64_t ts_mha_decode_workspace_size(int32_t n_seqs, int32_t n_q_heads, int32_t n_kv_heads,
+                                                int32_t head_dim, int32_t window, int32_t max_seqlen_k) {
+  const int rc = check_cache_shapes(n_q_heads, n_kv_heads, head_dim, 1.f, n_seqs, 1, 16,
+                                    (max_seqlen_k + 15) / 16 + 1, max_seqlen_k);
+  if (rc != TS_MHA_OK) return rc;
+  const tsmha::DecodePlan plan = tsmha::decode_plan(decode_args(n_q_heads, n_kv_heads, window, n_seqs, max_seqlen_k));
+  if (plan.n_splits < 0) return TS_MHA_ERR_BAD_SHAPE;
+  return plan.workspace_bytes;
+}
+
+extern "C" int ts_mha_decode_with_kvcache(const void* q, const void* k_cache, const void* v_cache,
+                                          const float* sinks, const int32_t* seqlens_k,
+                                          const int32_t* block_table, int32_t n_q_heads,
+                                          int32_t n_kv_heads, int32_t head_dim, int32_t window,
+                                          float softmax_scale, void* out, int32_t n_seqs,
+                                          int32_t n_pages, int32_t page_size, int32_t pages_per_seq,
+                                          int32_t max_seqlen_k, void* workspace,
+                                          int64_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !seqlens_k || !block_table || !out) return TS_MHA_ERR_NULL_ARG;
+  int rc = check_cache_shapes(n_q_heads, n_kv_heads, head_dim, softmax_scale, n_seqs, n_pages, page_size,
+                              pages_per_seq, max_seqlen_k);
+  if (rc != TS_MHA_OK) return rc;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(sinks, 4) || !aligned(seqlens_k, 4) || !aligned(block_table, 4) || !aligned(workspace, 256))
+    return TS_MHA_ERR_ALIGN;
+  tsmha::DecodeArgs a = decode_args(n_q_heads, n_kv_heads, window, n_seqs, max_seqlen_k);
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.sinks = sinks;
+  a.seqlens_k = seqlens_k;
+  a.block_table = block_table;
+  a.out = out;
+  a.softmax_scale = softmax_scale;
+  a.n_pages = n_pages;
+  a.page_size = page_size;
+  a.pages_per_seq = pages_per_seq;
+  const tsmha::DecodePlan plan = tsmha::decode_plan(a);
+  if (plan.n_splits < 0) return TS_MHA_ERR_BAD_SHAPE;
+  if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+    return TS_MHA_ERR_WORKSPACE;
+
+  rc = check_device();
+  if (rc != TS_MHA_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const char* dbg = getenv("TS_MHA_VALIDATE");
+  if (dbg && dbg[0] == '1' && n_seqs > 0) {
+    rc = validate_cache(seqlens_k, block_table, n_seqs, n_pages, page_size, pages_per_seq, max_seqlen_k, st);
+    if (rc != TS_MHA_OK) return rc;
+  }
+  if (n_seqs == 0) return TS_MHA_OK;
+  const hipError_t err = tsmha::launch_decode(a, plan, workspace, st);
+  if (err != hipSuccess) {
+    snprintf(g_launch_msg, sizeof g_launch_msg, "%s", hipGetErrorString(err));
+    return TS_MHA_ERR_LAUNCH;
+  }
+  return TS_MHA_OK;
+}
+
 extern "C" const char* ts_mha_strerror(int code) {
   switch (code) {
     case TS_MHA_OK: return "success";
     case TS_MHA_ERR_NULL_ARG: return "a required pointer argument is NULL";
     case TS_MHA_ERR_BAD_SHAPE:
       return "bad shape: heads must be > 0 with n_q_heads a multiple of n_kv_heads, n_seqs and "
-             "max_seqlen must be >= 0, and the launch grid must fit";
+             "max_seqlen must be >= 0, the launch grid must fit; for the cache calls page_size a power "
+             "of two >= 16, n_pages and pages_per_seq > 0, max_seqlen_k <= pages_per_seq * page_size";
     case TS_MHA_ERR_UNSUPPORTED:
       return "unsupported configuration: head_dim must be 64 and n_q_heads / n_kv_heads one of "
              "1, 2, 4, 8, 16";
     case TS_MHA_ERR_BAD_SCALE: return "softmax_scale must be finite and > 0";
     case TS_MHA_ERR_ALIGN:
-      return "misaligned pointer: q, k, v, out need 16-byte alignment, sinks and cu_seqlens 4-byte";
+      return "misaligned pointer: q, k, v (or the caches), out need 16-byte alignment, sinks, "
+             "cu_seqlens, seqlens_k and block_table 4-byte, the workspace 256-byte";
     case TS_MHA_ERR_NO_DEVICE: return "no HIP device is available";
     case TS_MHA_ERR_ARCH: return "the current HIP device is not a gfx950 (MI355X-class) GPU";
     case TS_MHA_ERR_LAUNCH: {
@@ -144,7 +262,11 @@ extern "C" const char* ts_mha_strerror(int code) {
       return msg;
     }
     case TS_MHA_ERR_SEQLENS:
-      return "cu_seqlens violates its contract (cu[0] == 0, non-decreasing, lengths <= max_seqlen)";
+      return "sequence lengths violate their contract (cu_seqlens: cu[0] == 0, non-decreasing, lengths <= "
+             "max_seqlen; seqlens_k: 0 <= length <= max_seqlen_k)";
+    case TS_MHA_ERR_WORKSPACE:
+      return "workspace missing or smaller than ts_mha_decode_workspace_size reports";
+    case TS_MHA_ERR_PAGES: return "a block-table entry a sequence needs is outside [0, n_pages)";
     default: return "unknown error";
   }
 }

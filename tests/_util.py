@@ -65,3 +65,38 @@ def rounding_bound(inp: dict, ref, lib=None):
     from oracle import oracle
     weighted_abs = oracle.prefill(*oracle_args(dict(inp, v=inp["v"].abs())), lib=lib)
     return 2.0 ** -8 * (1 + 2.0 ** -6) * (weighted_abs + 2.0 * np.abs(ref)) + 1e-6
+
+
+def cache_oracle_args(inp: dict):
+    """Arguments of oracle.cache_attend(...) for an input dict from workloads.make_cache_inputs."""
+    sinks = inp["sinks"]
+    return (bf16_bits(inp["q"]), bf16_bits(inp["k_cache"]), bf16_bits(inp["v_cache"]),
+            None if sinks is None else sinks.detach().cpu().numpy().astype(np.float32),
+            inp["cu_seqlens_q"].cpu().numpy().astype(np.int32),
+            inp["seqlens_k"].cpu().numpy().astype(np.int32),
+            inp["block_table"].cpu().numpy().astype(np.int32), inp["window"],
+            inp["softmax_scale"])
+
+
+def run_gpu_decode(inp: dict, out=None, stream=None, workspace=None, k_cache=None, v_cache=None):
+    """Run the decode kernels (through the C ABI) on a cache input dict; returns the GPU output."""
+    import sinks_ts_mha_amd as tm
+    dev = torch.device("cuda", 0)
+    kc = (inp["k_cache"] if k_cache is None else k_cache).to(dev)
+    vc = (inp["v_cache"] if v_cache is None else v_cache).to(dev)
+    sinks = None if inp["sinks"] is None else inp["sinks"].to(dev)
+    return tm.ts_mha_decode_with_kvcache(
+        inp["q"].to(dev), kc, vc, sinks, inp["seqlens_k"].to(dev), inp["block_table"].to(dev),
+        window=inp["window"], softmax_scale=inp["softmax_scale"], out=out,
+        max_seqlen_k=inp["max_seqlen_k"], workspace=workspace, stream=stream)
+
+
+def cache_rounding_bound(inp: dict, ref, lib=None):
+    """rounding_bound for the cache form: the same roundings (bf16 probabilities in the
+    numerator, fp32 denominator or its bf16 image, bf16 output), with sum_j p_j |v_jd|
+    from the oracle's cache form applied to |v|."""
+    from oracle import oracle
+    args = list(cache_oracle_args(inp))
+    args[2] = bf16_bits(inp["v_cache"].abs())
+    weighted_abs = oracle.cache_attend(*args, lib=lib)
+    return 2.0 ** -8 * (1 + 2.0 ** -6) * (weighted_abs + 2.0 * np.abs(ref)) + 1e-6

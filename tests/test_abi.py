@@ -21,7 +21,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["ts_mha_prefill", "ts_mha_strerror", "ts_mha_unmasked_pairs"]
+    assert declared_functions() == ["ts_mha_decode_with_kvcache", "ts_mha_decode_workspace_size",
+                                    "ts_mha_prefill", "ts_mha_strerror", "ts_mha_unmasked_pairs"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -134,3 +135,54 @@ def test_binding_rejects_cpu_tensors():
         tm.ts_mha_prefill(q, q[:, :1].contiguous(), q[:, :1].contiguous(), None, cu, max_seqlen=4)
     with pytest.raises(TypeError):
         tm.ts_mha_prefill(q.float(), q, q, None, cu, max_seqlen=4)
+
+
+# ---- decode against a paged KV cache
+
+def dcall(q=FAKE, kc=FAKE, vc=FAKE, sinks=None, lens=FAKE, table=FAKE, hq=64, hkv=8, d=64,
+          window=0, scale=0.125, out=FAKE * 2, n_seqs=64, n_pages=40000, page=16, pps=512,
+          max_k=8192, ws=FAKE * 4, ws_bytes=1 << 30, stream=None):
+    return tm.lib().ts_mha_decode_with_kvcache(q, kc, vc, sinks, lens, table, hq, hkv, d, window,
+                                               scale, out, n_seqs, n_pages, page, pps, max_k, ws,
+                                               ws_bytes, stream)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(kc=None), -1), (dict(vc=None), -1), (dict(lens=None), -1),
+    (dict(table=None), -1), (dict(out=None), -1),
+    (dict(hq=0), -2), (dict(hq=12, hkv=8), -2), (dict(n_seqs=-1), -2), (dict(max_k=-1), -2),
+    (dict(n_pages=0), -2), (dict(pps=0), -2), (dict(page=8), -2), (dict(page=24), -2),
+    (dict(page=0), -2), (dict(max_k=512 * 16 + 1), -2), (dict(page=1 << 20, hkv=64, hq=64), -2),
+    (dict(d=128), -3), (dict(hq=64, hkv=2), -3),
+    (dict(scale=0.0), -4), (dict(scale=float("nan")), -4),
+    (dict(q=FAKE + 8), -5), (dict(kc=FAKE + 4), -5), (dict(out=FAKE + 2), -5),
+    (dict(table=FAKE + 2), -5), (dict(ws=FAKE + 64), -5),
+    (dict(ws=None, n_seqs=1), -10), (dict(ws_bytes=1024, n_seqs=1), -10),
+])
+def test_decode_host_validation_codes(kw, code):
+    assert dcall(**kw) == code
+
+
+def test_decode_workspace_size():
+    ws = tm.ts_mha_decode_workspace_size
+    # many sequences with a short context: one chunk per sequence, no workspace
+    assert ws(256, 64, 8, 64, 0, 2048) == 0
+    assert ws(64, 64, 8, 64, 128, 8192) >= 0
+    # one long sequence is split into chunks whose partial rows need a workspace
+    big = ws(1, 64, 8, 64, 0, 65536)
+    assert big > 0 and big % 4 == 0
+    assert ws(1, 64, 8, 64, 0, 65536) == big  # a function of its arguments only
+    assert ws(0, 64, 8, 64, 0, 0) == 0
+    with pytest.raises(tm.TsMhaError):
+        ws(1, 64, 8, 128, 0, 1024)
+    with pytest.raises(tm.TsMhaError):
+        ws(1, 12, 8, 64, 0, 1024)
+
+
+def test_decode_validation_precedes_device_check():
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert dcall() == -6
+    assert dcall(n_seqs=0) == -6
+    assert dcall(n_seqs=1, max_k=65536, pps=4096, ws_bytes=1 << 30) == -6
+    assert dcall(ws=None, max_k=2048, n_seqs=256) == -6  # no workspace needed there
