@@ -3,6 +3,7 @@
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --sweep            # the chart family: one JSON line per point
     python bench.py --decode           # decode against a paged KV cache: one line per workload
+    python bench.py --prefill-kvcache  # new rows against a paged KV cache: one line per workload
 
 One step is one ts_mha_prefill call over the whole workload: every stage of the
 operation (tile walk, QK^T, mask, online softmax with sink, PV, epilogue) runs
@@ -22,6 +23,10 @@ figure is algorithmic HBM bytes per second (every visible cached key and value
 read once, q read, out written).  `value` uses the wall time of eager calls
 (host overhead included); `gpu_avg_us` and `frac_hbm` (against the 8 TB/s roof)
 use the same calls replayed from one captured HIP graph.
+
+--prefill-kvcache times ts_mha_prefill_with_kvcache (chunked prefill: new rows at
+the end of each sequence's cached keys) and reports TFLOP/s over the visible
+(query, key) pairs, as the main metric does, against the bf16 MFMA peak.
 
 Only one GPU is used; --gpus above 1 is refused.
 """
@@ -88,6 +93,17 @@ def decode_algorithmic_bytes(wl) -> int:
             + 4 * wl.n_seqs + 4 * pages + 4 * wl.n_q_heads)
 
 
+def cache_visible_pairs(wl) -> int:
+    """Visible (query, key) pairs per head of new rows at the end of each sequence's keys."""
+    total = 0
+    for q, L in zip(wl.q_lens, wl.k_lens):
+        off = L - q
+        for i in range(q):
+            n = off + i + 1
+            total += min(n, wl.window) if wl.window > 0 else n
+    return total
+
+
 def cpu_baseline(wl, inp, target_s: float):
     """Time the fp64 oracle on a strided row sample sized for about target_s seconds."""
     import numpy as np
@@ -148,6 +164,8 @@ def main():
                     help="time every chart point (sequence length x batch, full causal) instead")
     ap.add_argument("--decode", action="store_true",
                     help="time decode against a paged KV cache on its workloads instead")
+    ap.add_argument("--prefill-kvcache", action="store_true",
+                    help="time prefill of new rows against a paged KV cache instead")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {a.gpus} is not supported "
@@ -201,8 +219,48 @@ def main():
         del q, k, v, sinks, cu, out
         return inp, wall * 1e3 / steps, ev0.elapsed_time(ev1) / steps
 
+    if a.prefill_kvcache:
+        for name, wl in workloads.PREFILL_KV_WORKLOADS.items():
+            inp = workloads.make_cache_inputs(wl)
+            q, kc, vc = inp["q"].to(dev), inp["k_cache"].to(dev), inp["v_cache"].to(dev)
+            sinks = inp["sinks"].to(dev) if inp["sinks"] is not None else None
+            cuq, lens = inp["cu_seqlens_q"].to(dev), inp["seqlens_k"].to(dev)
+            table = inp["block_table"].to(dev)
+            out = torch.empty_like(q)
+
+            def pstep():
+                tm.ts_mha_prefill_with_kvcache(q, kc, vc, sinks, cuq, lens, table, window=wl.window,
+                                               softmax_scale=wl.softmax_scale, out=out,
+                                               max_seqlen_q=wl.max_seqlen_q,
+                                               max_seqlen_k=wl.max_seqlen_k, stream=stream)
+
+            for _ in range(a.warmup):
+                pstep()
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            ev0.record(stream)
+            for _ in range(a.steps):
+                pstep()
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            ms_step = (time.perf_counter() - t0) * 1e3 / a.steps
+            ms_gpu = ev0.elapsed_time(ev1) / a.steps
+            flops = 4 * wl.head_dim * wl.n_q_heads * cache_visible_pairs(wl)
+            print(json.dumps({"prefill_kvcache_point": name, "batch": wl.n_seqs,
+                              "q_len": wl.max_seqlen_q, "k_len": wl.max_seqlen_k,
+                              "window": wl.window, "page_size": wl.page_size,
+                              "value": round(flops / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                              "kernel_avg_us": round(ms_gpu * 1e3, 2),
+                              "frac": round(flops / (ms_gpu * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                              "flops": flops, "steps": a.steps, "warmup": a.warmup}), flush=True)
+            del q, kc, vc, sinks, cuq, lens, table, out
+            torch.cuda.empty_cache()
+        return
+
     if a.decode:
-        for name, wl in workloads.CACHE_WORKLOADS.items():
+        for name, wl in workloads.DECODE_WORKLOADS.items():
             inp = workloads.make_cache_inputs(wl)
             q, kc, vc = inp["q"].to(dev), inp["k_cache"].to(dev), inp["v_cache"].to(dev)
             sinks = inp["sinks"].to(dev) if inp["sinks"] is not None else None

@@ -4,8 +4,10 @@
  * The main operation: causal grouped-query attention over packed
  * variable-length sequences, with an optional sliding window and an optional
  * per-head attention sink (ts_mha_prefill).  Decode against a paged KV cache
- * (ts_mha_decode_with_kvcache) applies the same attention to one new query
- * row per sequence; it is declared further below.  ts_mha_prefill is the
+ * (ts_mha_decode_with_kvcache) and prefill of new rows against such a cache
+ * (ts_mha_prefill_with_kvcache) apply the same attention to query rows that
+ * sit at the end of each sequence's cached keys; they are declared further
+ * below.  ts_mha_prefill is the
  * `mha_prefill` public call listed in the
  * TokenSpeed-kernel README, section "Public API" (kept apart there from
  * `mha_prefill_with_kvcache`, so no cache is involved), for the GPT-OSS
@@ -62,7 +64,8 @@ extern "C" {
 #define TS_MHA_ERR_LAUNCH (-8)       /* the HIP launch failed; ts_mha_strerror adds the HIP error text */
 #define TS_MHA_ERR_SEQLENS (-9)      /* only with TS_MHA_VALIDATE=1 in the environment: cu_seqlens[0] != 0,
                                         cu_seqlens decreasing, or a length above max_seqlen; for the
-                                        cache call a seqlens_k entry outside [0, max_seqlen_k] */
+                                        cache calls a seqlens_k entry outside [0, max_seqlen_k] or
+                                        below the sequence's new-row count */
 #define TS_MHA_ERR_WORKSPACE (-10)   /* decode: workspace NULL or smaller than ts_mha_decode_workspace_size */
 #define TS_MHA_ERR_PAGES (-11)       /* only with TS_MHA_VALIDATE=1: a block-table entry that a sequence
                                         needs is outside [0, n_pages) */
@@ -112,6 +115,46 @@ const char* ts_mha_strerror(int code);
  *  length is negative.
  */
 int64_t ts_mha_unmasked_pairs(const int32_t* cu_seqlens_host, int32_t n_seqs, int32_t window);
+
+/*
+ * ts_mha_prefill_with_kvcache -- prefill of new query rows against a paged KV
+ * cache (chunked prefill): each sequence's new rows attend to all its cached
+ * keys, their own included.  The TokenSpeed-kernel README, section "Public
+ * API", lists `mha_prefill_with_kvcache` beside `mha_prefill`; the pages give
+ * no signature or layout.  Readings taken here (shared with
+ * ts_mha_decode_with_kvcache below):
+ *  - the cache already holds the new rows' own keys and values (the caller
+ *    writes them first); seqlens_k[b] counts every cached key of sequence b;
+ *  - the q_len = cu_seqlens_q[b+1] - cu_seqlens_q[b] new rows are the
+ *    sequence's last q_len positions: row i sits at p = seqlens_k[b] - q_len + i
+ *    (the causal diagonal aligned to the bottom right);
+ *  - key position j lives in page block_table[b][j / page_size], slot
+ *    j % page_size, of k_cache / v_cache [n_pages][page_size][n_kv_heads][64];
+ *  - visible keys, sink, scale and head mapping are those of ts_mha_prefill at
+ *    position p.  With q_len == seqlens_k[b] the result is ts_mha_prefill's.
+ *
+ *  q, out        device, bf16 [Tq][n_q_heads][64] packed by cu_seqlens_q, 16-byte
+ *                aligned; out fully overwritten, no overlap with any input
+ *  k_cache, v_cache, sinks, block_table, n_pages, page_size, pages_per_seq
+ *                as for ts_mha_decode_with_kvcache
+ *  cu_seqlens_q  device, int32 [n_seqs + 1]: cu[0] = 0, non-decreasing, each
+ *                length <= max_seqlen_q
+ *  seqlens_k     device, int32 [n_seqs]: q_len_b <= seqlens_k[b] <= max_seqlen_k
+ *  max_seqlen_q  >= every new-row count, <= max_seqlen_k (sizes the launch)
+ *  max_seqlen_k  >= every seqlens_k[b], <= pages_per_seq * page_size and <= 2^30
+ *
+ *  Out-of-contract lengths or table entries never move a read outside the
+ *  block table or the cache pool (page ids are clamped, keys at or past
+ *  seqlens_k[b] read as zeros) but give meaningless rows; TS_MHA_VALIDATE=1
+ *  checks them first.  Returns TS_MHA_OK or a TS_MHA_ERR_* code.
+ */
+int ts_mha_prefill_with_kvcache(const void* q, const void* k_cache, const void* v_cache,
+                                const float* sinks, const int32_t* cu_seqlens_q,
+                                const int32_t* seqlens_k, const int32_t* block_table,
+                                int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                int32_t window, float softmax_scale, void* out, int32_t n_seqs,
+                                int32_t n_pages, int32_t page_size, int32_t pages_per_seq,
+                                int32_t max_seqlen_q, int32_t max_seqlen_k, void* stream);
 
 /*
  * ts_mha_decode_with_kvcache -- decode attention against a paged KV cache:

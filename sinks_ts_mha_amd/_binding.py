@@ -52,6 +52,10 @@ def lib() -> ctypes.CDLL:
                                                  ctypes.c_float, vp, i32, i32, i32, i32, i32, vp,
                                                  i64, vp]
         L.ts_mha_decode_with_kvcache.restype = ctypes.c_int
+        L.ts_mha_prefill_with_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                                  ctypes.c_float, vp, i32, i32, i32, i32, i32, i32,
+                                                  vp]
+        L.ts_mha_prefill_with_kvcache.restype = ctypes.c_int
         L.ts_mha_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
         L.ts_mha_decode_workspace_size.restype = i64
         _lib = L
@@ -152,6 +156,82 @@ def _stream_handle(stream, dev):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _check_cache(q, k_cache, v_cache, sinks, seqlens_k, block_table, n_seqs):
+    dev = q.device
+    _check_tensor("q", q, torch.bfloat16, 3, dev)
+    _check_tensor("k_cache", k_cache, torch.bfloat16, 4, dev)
+    _check_tensor("v_cache", v_cache, torch.bfloat16, 4, dev)
+    _check_tensor("seqlens_k", seqlens_k, torch.int32, 1, dev)
+    _check_tensor("block_table", block_table, torch.int32, 2, dev)
+    if not q.is_cuda:
+        raise ValueError("q must be a GPU tensor")
+    if v_cache.shape != k_cache.shape or k_cache.shape[3] != q.shape[2]:
+        raise ValueError("k_cache and v_cache must both be [n_pages, page_size, Hkv, D]")
+    if seqlens_k.shape != (n_seqs,) or block_table.shape[0] != n_seqs:
+        raise ValueError("seqlens_k must be [n_seqs] and block_table [n_seqs, pages_per_seq]")
+    if sinks is not None:
+        _check_tensor("sinks", sinks, torch.float32, 1, dev)
+        if sinks.shape != (q.shape[1],):
+            raise ValueError("sinks must be [Hq]")
+
+
+def _check_out(out, q, inputs):
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor("out", out, torch.bfloat16, 3, q.device)
+        if out.shape != q.shape:
+            raise ValueError("out must be shaped like q")
+    for name, t in inputs:
+        if t is not None and _overlaps(out, t):
+            raise ValueError(f"out must not overlap {name}")
+    return out
+
+
+def ts_mha_prefill_with_kvcache(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                sinks, cu_seqlens_q: torch.Tensor, seqlens_k: torch.Tensor,
+                                block_table: torch.Tensor, window: int = 0,
+                                softmax_scale: float | None = None, out=None,
+                                max_seqlen_q: int | None = None, max_seqlen_k: int | None = None,
+                                stream=None) -> torch.Tensor:
+    """Prefill of new query rows against a paged KV cache (chunked prefill).
+
+    q [Tq, Hq, 64] bf16 packed by cu_seqlens_q (int32 [n_seqs + 1]); the caches
+    [n_pages, page_size, Hkv, 64] bf16 already hold the new rows' keys and values;
+    seqlens_k int32 [n_seqs] counts every cached key; block_table int32
+    [n_seqs, pages_per_seq].  Row i of a sequence with q_len new rows sits at
+    position seqlens_k - q_len + i.  max_seqlen_q / max_seqlen_k size the launch;
+    if omitted they are read back (synchronising).
+    """
+    dev = q.device
+    _check_tensor("cu_seqlens_q", cu_seqlens_q, torch.int32, 1, dev)
+    n_seqs = cu_seqlens_q.numel() - 1
+    _check_cache(q, k_cache, v_cache, sinks, seqlens_k, block_table, n_seqs)
+    out = _check_out(out, q, (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                              ("cu_seqlens_q", cu_seqlens_q), ("seqlens_k", seqlens_k),
+                              ("block_table", block_table), ("sinks", sinks)))
+    Tq, hq, D = q.shape
+    n_pages, page_size, hkv, _ = k_cache.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / (D ** 0.5)
+    if Tq == 0:
+        return out
+    if max_seqlen_q is None:
+        cu = cu_seqlens_q.cpu()
+        max_seqlen_q = int((cu[1:] - cu[:-1]).max()) if n_seqs > 0 else 0
+    if max_seqlen_k is None:
+        max_seqlen_k = int(seqlens_k.max().cpu()) if n_seqs > 0 else 0
+    rc = lib().ts_mha_prefill_with_kvcache(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        None if sinks is None else sinks.data_ptr(), cu_seqlens_q.data_ptr(), seqlens_k.data_ptr(),
+        block_table.data_ptr(), hq, hkv, D, int(window), float(softmax_scale), out.data_ptr(),
+        n_seqs, n_pages, page_size, block_table.shape[1], int(max_seqlen_q), int(max_seqlen_k),
+        _stream_handle(stream, dev))
+    if rc != TS_MHA_OK:
+        raise TsMhaError(rc, ts_mha_strerror(rc))
+    return out
+
+
 def ts_mha_decode_workspace_size(n_seqs: int, n_q_heads: int, n_kv_heads: int, head_dim: int = 64,
                                  window: int = 0, max_seqlen_k: int = 0) -> int:
     """Workspace bytes a decode call with these arguments needs (0: none)."""
@@ -177,33 +257,12 @@ def ts_mha_decode_with_kvcache(q: torch.Tensor, k_cache: torch.Tensor, v_cache: 
     allocated here.  Runs on `stream` (default: torch's current stream).
     """
     dev = q.device
-    _check_tensor("q", q, torch.bfloat16, 3, dev)
-    _check_tensor("k_cache", k_cache, torch.bfloat16, 4, dev)
-    _check_tensor("v_cache", v_cache, torch.bfloat16, 4, dev)
-    _check_tensor("seqlens_k", seqlens_k, torch.int32, 1, dev)
-    _check_tensor("block_table", block_table, torch.int32, 2, dev)
-    if not q.is_cuda:
-        raise ValueError("q must be a GPU tensor")
     B, hq, D = q.shape
-    n_pages, page_size, hkv, Dk = k_cache.shape
-    if v_cache.shape != k_cache.shape or Dk != D:
-        raise ValueError("k_cache and v_cache must both be [n_pages, page_size, Hkv, D]")
-    if seqlens_k.shape != (B,) or block_table.shape[0] != B:
-        raise ValueError("seqlens_k must be [B] and block_table [B, pages_per_seq]")
-    if sinks is not None:
-        _check_tensor("sinks", sinks, torch.float32, 1, dev)
-        if sinks.shape != (hq,):
-            raise ValueError("sinks must be [Hq]")
-    if out is None:
-        out = torch.empty_like(q)
-    else:
-        _check_tensor("out", out, torch.bfloat16, 3, dev)
-        if out.shape != q.shape:
-            raise ValueError("out must be shaped like q")
-    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seqlens_k", seqlens_k),
-                    ("block_table", block_table)) + ((("sinks", sinks),) if sinks is not None else ()):
-        if _overlaps(out, t):
-            raise ValueError(f"out must not overlap {name}")
+    _check_cache(q, k_cache, v_cache, sinks, seqlens_k, block_table, B)
+    n_pages, page_size, hkv, _ = k_cache.shape
+    out = _check_out(out, q, (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                              ("seqlens_k", seqlens_k), ("block_table", block_table),
+                              ("sinks", sinks)))
     if softmax_scale is None:
         softmax_scale = 1.0 / (D ** 0.5)
     if B == 0:
@@ -232,3 +291,4 @@ def ts_mha_decode_with_kvcache(q: torch.Tensor, k_cache: torch.Tensor, v_cache: 
 # The operations' names in the public API the pages list.
 mha_prefill = ts_mha_prefill
 mha_decode_with_kvcache = ts_mha_decode_with_kvcache
+mha_prefill_with_kvcache = ts_mha_prefill_with_kvcache

@@ -9,17 +9,24 @@ namespace tsmha {
 
 struct PrefillArgs {
   const void* q;             // bf16 [T][n_q_heads][64]
-  const void* k;             // bf16 [T][n_kv_heads][64]
-  const void* v;             // bf16 [T][n_kv_heads][64]
+  const void* k;             // bf16 [T][n_kv_heads][64], or the k cache (block_table set)
+  const void* v;             // bf16 [T][n_kv_heads][64], or the v cache
   const float* sinks;        // fp32 [n_q_heads] or nullptr
-  const int32_t* cu_seqlens; // int32 [n_seqs + 1]
+  const int32_t* cu_seqlens; // int32 [n_seqs + 1], the new query rows
   void* out;                 // bf16 [T][n_q_heads][64]
   int32_t n_q_heads;
   int32_t n_kv_heads;
   int32_t window;            // <= 0: none
   float softmax_scale;
   int32_t n_seqs;
-  int32_t max_seqlen;
+  int32_t max_seqlen;        // longest run of new query rows
+  // paged K/V (prefill of new rows against a cache); block_table == nullptr
+  // means k and v are packed like q
+  const int32_t* seqlens_k = nullptr;    // int32 [n_seqs]
+  const int32_t* block_table = nullptr;  // int32 [n_seqs][pages_per_seq]
+  int32_t n_pages = 0;
+  int32_t page_size = 0;                 // a power of two >= 16
+  int32_t pages_per_seq = 0;
 };
 
 // Number of work-groups the launch will use (0 means nothing to launch), or

@@ -67,20 +67,14 @@
 
 #include <type_traits>
 
+#include "cdna4.h"
+
 namespace tsmha {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+using namespace cdna4;
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kD = 64;                        // head_dim
 constexpr int kBK = 64;                       // keys per LDS tile
@@ -91,9 +85,7 @@ constexpr int kRowBytes = kD * 2;             // one K or V row in bytes
 constexpr int kChunks = kRowBytes / 16;       // 16-byte chunks per row
 constexpr int kTileChunks = kBK * kChunks;    // 16-byte chunks per tile
 constexpr int kTileBytes = kTileChunks * 16;
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kFastSumLimit = 1.8446744e19f;  // 2^64: largest row sum the fast pass keeps
-constexpr int kBufferConfig = 0x00020000;     // raw buffer descriptor word 3 (32-bit data)
 constexpr int kSlots = 2;                     // LDS buffers for K and for V tiles
 
 
@@ -109,18 +101,17 @@ struct KParams {
   int32_t n_pblocks;
   int32_t window;
   float c;  // softmax_scale * log2(e)
+  // paged K/V only: k and v are the caches [n_pages][page_size][n_kv_heads][64]
+  const int32_t* seqlens_k;    // cached keys per sequence, the new rows' own included
+  const int32_t* block_table;  // [n_seqs][pages_per_seq] page ids
+  int64_t page_elems;          // bf16 elements per page
+  int32_t page_bytes;
+  int32_t page_shift;
+  int32_t pages_per_seq;
+  int32_t n_pages;
 };
 
 namespace {
-
-// Position of 16-byte chunk `ch` of tile row `row` in LDS.  The LDS serves 256
-// bytes (64 banks of 4 bytes) per cycle, i.e. two 128-byte tile rows, so rows of
-// equal parity collide unless their chunks differ.  The XOR key uses row bits 1
-// (as chunk bit 2) and 2..3 (as chunk bits 0..1): 16 consecutive rows reading
-// one logical chunk (the K operand reads) and 4 consecutive rows reading 4
-// adjacent chunks (the V transpose reads) both hit 16 distinct bank groups.
-__device__ __forceinline__ int swz_key(int row) { return ((row & 2) << 1) | ((row >> 2) & 3); }
-__device__ __forceinline__ int swz(int row, int ch) { return row * kChunks + (ch ^ swz_key(row)); }
 
 // max / sum of x over the lane pair (l, l ^ 32): v_permlane32_swap hands each
 // lane both halves of the pair.
@@ -144,50 +135,9 @@ __device__ __forceinline__ float max16(const f32x16& a) {
   return fmaxf(fmaxf(x, a[14]), fmaxf(y, a[15]));
 }
 
-// Raw buffer descriptor (base, stride 0, byte range n) in scalar registers.
-__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, int n) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
-  r[2] = __builtin_amdgcn_readfirstlane(n);
-  r[3] = kBufferConfig;
-  return r;
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const u32x4* p) {
-  return (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)p);
-}
-
-// One wave-wide 16-byte-per-lane load from a buffer straight into LDS: lane i's
-// 16 bytes land at lds + 16 i (lds must be wave-uniform).  Written as inline
-// assembly so that the compiler does not treat later LDS reads of other ring
-// slots as possibly overwritten by this load and stall them on its completion;
-// the kernel orders these loads itself (wait_vmem + barrier).  M0 carries the
-// LDS address and is used by nothing else in these kernels.
-__device__ __forceinline__ void lds_dma16(uint32_t lds, const i32x4& rsrc, int voffset) {
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds"
-      :
-      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voffset), "s"(rsrc)
-      : "m0");
-#pragma clang diagnostic pop
-}
-
-// Wait until at most N vector-memory operations of this wave are in flight.
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N <= 15, "vmcnt field");
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-
 }  // namespace
 
-template <int G, bool WINDOWED>
+template <int G, bool WINDOWED, bool PAGED>
 __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   constexpr int P = kRows / G;  // positions per work-group
   __shared__ u32x4 lds_k[kSlots * kTileChunks];
@@ -210,6 +160,10 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   const int L = p.cu[b + 1] - s;
   const int p0 = pblk * P;
   if (p0 >= L) return;
+  // With a KV cache the L new rows are the last L of the sequence's Lk cached
+  // positions: query row i sits at key position qoff + i.
+  const int Lk = PAGED ? p.seqlens_k[b] : L;
+  const int qoff = PAGED ? max(Lk - L, 0) : 0;
 
   // The prologue (address set-up and the first loads) runs at raised wave
   // priority: a work-group starting next to a busy one on its compute unit
@@ -225,8 +179,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   const int half16 = (lane >> 4) & 1;
   const float c = p.c;
 
-  const int last = min(L, p0 + P) - 1;
-  const int first = WINDOWED ? max(0, p0 - p.window + 1) : 0;
+  const int last = qoff + min(L, p0 + P) - 1;
+  const int first = WINDOWED ? max(0, qoff + p0 - p.window + 1) : 0;
   const int kt0 = first / kBK;
   const int kt1 = last / kBK;
 
@@ -242,21 +196,53 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   const int tile_stride = kBK * Hkv * kRowBytes;
   const i32x4 rk = buffer_rsrc(p.k + seq_elems, nbytes);
   const i32x4 rv = buffer_rsrc(p.v + seq_elems, nbytes);
-  int voff[2];
+  int voff[2], pvoff[2];
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
     const int row = (2 * w + it) * 8 + (lane >> 3);
     const int data_ch = (lane & 7) ^ swz_key(row);
     voff[it] = (row * Hkv + g) * kRowBytes + data_ch * 16;
+    pvoff[it] = g * kRowBytes + data_ch * 16;
   }
   const uint32_t lds_k_base = lds_addr(lds_k) + w * 2048;  // this wave's part of slot 0
   const uint32_t lds_v_base = lds_addr(lds_v) + w * 2048;
+  // Paged K/V: wave w loads rows 16 w .. 16 w + 15 of a tile, which lie in one
+  // page (pages hold at least 16 keys).  Lane l of pgv holds that page for
+  // tile pg_base - l; the walk only goes down, so the 64 ids are refilled when
+  // it leaves them (and when the exact redo restarts from the top).  Page ids
+  // are clamped into the table and the pool; keys at or past Lk read as zeros.
+  const int32_t* brow = PAGED ? p.block_table + (int64_t)b * p.pages_per_seq : nullptr;
+  const int pmask = PAGED ? (1 << p.page_shift) - 1 : 0;
+  int pg_base = -(1 << 30);
+  int pgv = 0;
+  auto tile_page = [&](int t) -> int {
+    if ((unsigned)(pg_base - t) >= 64u) {
+      pg_base = t;
+      const int tt = t - lane;
+      const int pi = tt >= 0 ? min((tt * kBK + 16 * w) >> p.page_shift, p.pages_per_seq - 1) : 0;
+      pgv = min(max(brow[pi], 0), p.n_pages - 1);
+    }
+    return __builtin_amdgcn_readlane(pgv, pg_base - t);
+  };
   auto issue_tile = [&](int t, int buf) {
-    const int off = t * tile_stride;  // carried in the VGPR offset, which the range check covers
+    if constexpr (PAGED) {
+      const int64_t page_off = (int64_t)tile_page(t) * p.page_elems;
+      const i32x4 rkp = buffer_rsrc(p.k + page_off, p.page_bytes);
+      const i32x4 rvp = buffer_rsrc(p.v + page_off, p.page_bytes);
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      lds_dma16(lds_k_base + buf * kTileBytes + it * 1024, rk, off + voff[it]);
-      lds_dma16(lds_v_base + buf * kTileBytes + it * 1024, rv, off + voff[it]);
+      for (int it = 0; it < 2; ++it) {
+        const int key = t * kBK + (2 * w + it) * 8 + (lane >> 3);
+        const int vo = key < Lk ? (key & pmask) * Hkv * kRowBytes + pvoff[it] : p.page_bytes;
+        lds_dma16(lds_k_base + buf * kTileBytes + it * 1024, rkp, vo);
+        lds_dma16(lds_v_base + buf * kTileBytes + it * 1024, rvp, vo);
+      }
+    } else {
+      const int off = t * tile_stride;  // carried in the VGPR offset, which the range check covers
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        lds_dma16(lds_k_base + buf * kTileBytes + it * 1024, rk, off + voff[it]);
+        lds_dma16(lds_v_base + buf * kTileBytes + it * 1024, rv, off + voff[it]);
+      }
     }
   };
   // Tiles are walked from the last (the diagonal) back to the first.  The
@@ -346,7 +332,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     f32x16 acc = {};
     if constexpr (MASKED) {
-      const int di = pos[nb] - k0 - 4 * hi;
+      const int di = qoff + pos[nb] - k0 - 4 * hi;
       const int dw = di - p.window;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -504,8 +490,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   // the remaining probabilities are never below their streaming-softmax
   // values.  The runs are separate loops so that each loop body holds one
   // kind of tile.
-  const int ktB = max(kt0, min(kt1 + 1, (p0 + 1) / kBK));  // first tile with k0 + kBK - 1 > p0
-  const int xa = p0 + P - p.window;  // first tile with k0 >= xa: all its keys inside every window
+  const int ktB = max(kt0, min(kt1 + 1, (qoff + p0 + 1) / kBK));  // first tile with k0 + kBK - 1 > qoff + p0
+  const int xa = qoff + p0 + P - p.window;  // first tile with k0 >= xa: all its keys inside every window
   const int ktA = (WINDOWED && xa > 0) ? min(ktB, max(kt0, (xa + kBK - 1) / kBK)) : kt0;
   auto walk = [&](auto tile_fn, auto masked_tag, int kt_hi, int kt_lo) {
     for (int kt = kt_hi; kt >= kt_lo; --kt) {
@@ -596,11 +582,19 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
 namespace {
 
 template <int G>
-hipError_t launch_group(const KParams& kp, int64_t grid, bool windowed, hipStream_t stream) {
-  if (windowed)
-    hipLaunchKernelGGL((prefill_fwd_d64<G, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, kp);
-  else
-    hipLaunchKernelGGL((prefill_fwd_d64<G, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, kp);
+hipError_t launch_group(const KParams& kp, int64_t grid, bool windowed, bool paged, hipStream_t stream) {
+  const dim3 gd((unsigned)grid), bd(kThreads);
+  if (paged) {
+    if (windowed)
+      hipLaunchKernelGGL((prefill_fwd_d64<G, true, true>), gd, bd, 0, stream, kp);
+    else
+      hipLaunchKernelGGL((prefill_fwd_d64<G, false, true>), gd, bd, 0, stream, kp);
+  } else {
+    if (windowed)
+      hipLaunchKernelGGL((prefill_fwd_d64<G, true, false>), gd, bd, 0, stream, kp);
+    else
+      hipLaunchKernelGGL((prefill_fwd_d64<G, false, false>), gd, bd, 0, stream, kp);
+  }
   return hipGetLastError();
 }
 
@@ -614,7 +608,8 @@ int64_t pblocks(const PrefillArgs& a) {
 
 int64_t prefill_grid_size(const PrefillArgs& a) {
   // each sequence's K (or V) rows must be addressable by one buffer descriptor
-  if (((int64_t)a.max_seqlen + kBK) * a.n_kv_heads * kRowBytes > 0x7fffffffLL) return -1;
+  // (a cache is addressed page by page instead)
+  if (!a.block_table && ((int64_t)a.max_seqlen + kBK) * a.n_kv_heads * kRowBytes > 0x7fffffffLL) return -1;
   // and its query rows, including a position block's rows past the end
   if (((int64_t)a.max_seqlen + kRows) * a.n_q_heads * kRowBytes > 0x7fffffffLL) return -1;
   const int64_t n = pblocks(a) * (int64_t)a.n_seqs * (int64_t)a.n_kv_heads;
@@ -637,14 +632,22 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   kp.n_pblocks = (int32_t)pblocks(a);
   kp.window = a.window > 0 ? a.window : 0;
   kp.c = (float)((double)a.softmax_scale * 1.4426950408889634);
+  kp.seqlens_k = a.seqlens_k;
+  kp.block_table = a.block_table;
+  kp.page_elems = (int64_t)a.page_size * a.n_kv_heads * kD;
+  kp.page_bytes = a.page_size * a.n_kv_heads * kRowBytes;
+  kp.page_shift = a.page_size > 0 ? __builtin_ctz((unsigned)a.page_size) : 0;
+  kp.pages_per_seq = a.pages_per_seq;
+  kp.n_pages = a.n_pages;
   const bool windowed = a.window > 0;
+  const bool paged = a.block_table != nullptr;
   (void)hipGetLastError();  // start from a clean per-thread error state
   switch (a.n_q_heads / a.n_kv_heads) {
-    case 1: return launch_group<1>(kp, grid, windowed, stream);
-    case 2: return launch_group<2>(kp, grid, windowed, stream);
-    case 4: return launch_group<4>(kp, grid, windowed, stream);
-    case 8: return launch_group<8>(kp, grid, windowed, stream);
-    case 16: return launch_group<16>(kp, grid, windowed, stream);
+    case 1: return launch_group<1>(kp, grid, windowed, paged, stream);
+    case 2: return launch_group<2>(kp, grid, windowed, paged, stream);
+    case 4: return launch_group<4>(kp, grid, windowed, paged, stream);
+    case 8: return launch_group<8>(kp, grid, windowed, paged, stream);
+    case 16: return launch_group<16>(kp, grid, windowed, paged, stream);
     default: return hipErrorInvalidValue;
   }
 }

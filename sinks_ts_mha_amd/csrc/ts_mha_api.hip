@@ -98,6 +98,24 @@ int validate_cache(const int32_t* seqlens_k, const int32_t* block_table, int32_t
   return TS_MHA_OK;
 }
 
+// Debug mode for the prefill with a cache: every sequence has at least as many
+// cached keys as new rows.
+int validate_rows_fit(const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int32_t n_seqs,
+                      hipStream_t stream) {
+  std::vector<int32_t> cu((size_t)n_seqs + 1), lens((size_t)n_seqs);
+  if (hipMemcpyAsync(cu.data(), cu_seqlens_q, sizeof(int32_t) * cu.size(), hipMemcpyDeviceToHost, stream) !=
+          hipSuccess ||
+      hipMemcpyAsync(lens.data(), seqlens_k, sizeof(int32_t) * lens.size(), hipMemcpyDeviceToHost, stream) !=
+          hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess) {
+    snprintf(g_launch_msg, sizeof g_launch_msg, "%s", hipGetErrorString(hipGetLastError()));
+    return TS_MHA_ERR_LAUNCH;
+  }
+  for (int32_t b = 0; b < n_seqs; ++b)
+    if (cu[b + 1] - cu[b] > lens[b]) return TS_MHA_ERR_SEQLENS;
+  return TS_MHA_OK;
+}
+
 bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
 // Checks shared by the cache calls; TS_MHA_OK when the shapes are acceptable.
@@ -172,6 +190,64 @@ extern "C" int ts_mha_prefill(const void* q, const void* k, const void* v, const
   }
   if (grid == 0) return TS_MHA_OK;
 
+  const hipError_t err = tsmha::launch_prefill(a, st);
+  if (err != hipSuccess) {
+    snprintf(g_launch_msg, sizeof g_launch_msg, "%s", hipGetErrorString(err));
+    return TS_MHA_ERR_LAUNCH;
+  }
+  return TS_MHA_OK;
+}
+
+extern "C" int ts_mha_prefill_with_kvcache(const void* q, const void* k_cache, const void* v_cache,
+                                           const float* sinks, const int32_t* cu_seqlens_q,
+                                           const int32_t* seqlens_k, const int32_t* block_table,
+                                           int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                           int32_t window, float softmax_scale, void* out, int32_t n_seqs,
+                                           int32_t n_pages, int32_t page_size, int32_t pages_per_seq,
+                                           int32_t max_seqlen_q, int32_t max_seqlen_k, void* stream) {
+  if (!q || !k_cache || !v_cache || !cu_seqlens_q || !seqlens_k || !block_table || !out)
+    return TS_MHA_ERR_NULL_ARG;
+  int rc = check_cache_shapes(n_q_heads, n_kv_heads, head_dim, softmax_scale, n_seqs, n_pages, page_size,
+                              pages_per_seq, max_seqlen_k);
+  if (rc != TS_MHA_OK) return rc;
+  if (max_seqlen_q < 0 || max_seqlen_q > max_seqlen_k) return TS_MHA_ERR_BAD_SHAPE;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(sinks, 4) || !aligned(cu_seqlens_q, 4) || !aligned(seqlens_k, 4) || !aligned(block_table, 4))
+    return TS_MHA_ERR_ALIGN;
+
+  tsmha::PrefillArgs a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.sinks = sinks;
+  a.cu_seqlens = cu_seqlens_q;
+  a.out = out;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.window = window;
+  a.softmax_scale = softmax_scale;
+  a.n_seqs = n_seqs;
+  a.max_seqlen = max_seqlen_q;
+  a.seqlens_k = seqlens_k;
+  a.block_table = block_table;
+  a.n_pages = n_pages;
+  a.page_size = page_size;
+  a.pages_per_seq = pages_per_seq;
+  const int64_t grid = tsmha::prefill_grid_size(a);
+  if (grid < 0) return TS_MHA_ERR_BAD_SHAPE;
+
+  rc = check_device();
+  if (rc != TS_MHA_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const char* dbg = getenv("TS_MHA_VALIDATE");
+  if (dbg && dbg[0] == '1' && n_seqs > 0) {
+    rc = validate_seqlens(cu_seqlens_q, n_seqs, max_seqlen_q, st);
+    if (rc == TS_MHA_OK)
+      rc = validate_cache(seqlens_k, block_table, n_seqs, n_pages, page_size, pages_per_seq, max_seqlen_k, st);
+    if (rc == TS_MHA_OK) rc = validate_rows_fit(cu_seqlens_q, seqlens_k, n_seqs, st);
+    if (rc != TS_MHA_OK) return rc;
+  }
+  if (grid == 0) return TS_MHA_OK;
   const hipError_t err = tsmha::launch_prefill(a, st);
   if (err != hipSuccess) {
     snprintf(g_launch_msg, sizeof g_launch_msg, "%s", hipGetErrorString(err));

@@ -24,7 +24,8 @@ pages each, and the block table rows are padded with -1.  The pool holds
 `spare_pages` more pages than the sequences use.  The decode shapes follow the
 GPT-OSS layers of the same pages (64 q / 8 KV heads, head_dim 64, sinks, full and
 window-128 layers); the pages give no decode batch or context length, so the
-benchmark takes batch 64 at 8K context and batch 1 at 64K.
+benchmark takes batch 64 at 8K context and batch 1 at 64K, and for prefill
+against a cache 4 sequences of 2048 new rows at 8K context.
 """
 from __future__ import annotations
 
@@ -191,7 +192,7 @@ def decode(k_lens, n_q_heads=64, n_kv_heads=8, window=0, page_size=16, sinks=Tru
                          window=window, sinks=sinks, seed=seed, **kw)
 
 
-CACHE_WORKLOADS = {
+DECODE_WORKLOADS = {
     "decode_b64_k8192": decode(
         (8192,) * 64, name="decode_b64_k8192",
         notes="GPT-OSS full layer, decode: 64 sequences x 8192 cached keys, page 16, sinks"),
@@ -202,6 +203,20 @@ CACHE_WORKLOADS = {
         (65536,), name="decode_b1_k65536",
         notes="one long sequence, decode: 65536 cached keys, page 16, sinks"),
 }
+
+
+# Chunked prefill against a cache: 2048 new rows per sequence on top of 6144
+# cached positions (8192 keys in all), the GPT-OSS full and window-128 layers.
+PREFILL_KV_WORKLOADS = {
+    "prefill_kv_b4_q2048_k8192": CacheWorkload(
+        "prefill_kv_b4_q2048_k8192", (2048,) * 4, (8192,) * 4, 64, 8, page_size=16,
+        notes="chunked prefill: 4 sequences x 2048 new rows against 8192 cached keys, page 16"),
+    "prefill_kv_b4_q2048_k8192_window128": CacheWorkload(
+        "prefill_kv_b4_q2048_k8192_window128", (2048,) * 4, (8192,) * 4, 64, 8, page_size=16,
+        window=128, notes="chunked prefill, window-128 layer: 4 x 2048 new rows, 8192 cached keys"),
+}
+
+CACHE_WORKLOADS = {**DECODE_WORKLOADS, **PREFILL_KV_WORKLOADS}
 
 
 def make_cache_inputs(wl: CacheWorkload, seed: int | None = None) -> dict:

@@ -100,3 +100,16 @@ def cache_rounding_bound(inp: dict, ref, lib=None):
     args[2] = bf16_bits(inp["v_cache"].abs())
     weighted_abs = oracle.cache_attend(*args, lib=lib)
     return 2.0 ** -8 * (1 + 2.0 ** -6) * (weighted_abs + 2.0 * np.abs(ref)) + 1e-6
+
+
+def run_gpu_prefill_kv(inp: dict, out=None, stream=None, k_cache=None, v_cache=None):
+    """Run the prefill against a paged cache (through the C ABI); returns the GPU output."""
+    import sinks_ts_mha_amd as tm
+    dev = torch.device("cuda", 0)
+    kc = (inp["k_cache"] if k_cache is None else k_cache).to(dev)
+    vc = (inp["v_cache"] if v_cache is None else v_cache).to(dev)
+    sinks = None if inp["sinks"] is None else inp["sinks"].to(dev)
+    return tm.ts_mha_prefill_with_kvcache(
+        inp["q"].to(dev), kc, vc, sinks, inp["cu_seqlens_q"].to(dev), inp["seqlens_k"].to(dev),
+        inp["block_table"].to(dev), window=inp["window"], softmax_scale=inp["softmax_scale"],
+        out=out, max_seqlen_q=inp["max_seqlen_q"], max_seqlen_k=inp["max_seqlen_k"], stream=stream)

@@ -22,7 +22,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["ts_mha_decode_with_kvcache", "ts_mha_decode_workspace_size",
-                                    "ts_mha_prefill", "ts_mha_strerror", "ts_mha_unmasked_pairs"]
+                                    "ts_mha_prefill", "ts_mha_prefill_with_kvcache", "ts_mha_strerror",
+                                    "ts_mha_unmasked_pairs"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -186,3 +187,38 @@ def test_decode_validation_precedes_device_check():
     assert dcall(n_seqs=0) == -6
     assert dcall(n_seqs=1, max_k=65536, pps=4096, ws_bytes=1 << 30) == -6
     assert dcall(ws=None, max_k=2048, n_seqs=256) == -6  # no workspace needed there
+
+
+# ---- prefill of new rows against a paged KV cache
+
+def pcall(q=FAKE, kc=FAKE, vc=FAKE, sinks=None, cu=FAKE, lens=FAKE, table=FAKE, hq=64, hkv=8, d=64,
+          window=0, scale=0.125, out=FAKE * 2, n_seqs=4, n_pages=4000, page=16, pps=512,
+          max_q=2048, max_k=8192, stream=None):
+    return tm.lib().ts_mha_prefill_with_kvcache(q, kc, vc, sinks, cu, lens, table, hq, hkv, d, window,
+                                                scale, out, n_seqs, n_pages, page, pps, max_q, max_k,
+                                                stream)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(kc=None), -1), (dict(vc=None), -1), (dict(cu=None), -1),
+    (dict(lens=None), -1), (dict(table=None), -1), (dict(out=None), -1),
+    (dict(hq=0), -2), (dict(hq=12, hkv=8), -2), (dict(n_seqs=-1), -2), (dict(max_k=-1), -2),
+    (dict(max_q=-1), -2), (dict(max_q=8193), -2), (dict(page=8), -2), (dict(n_pages=0), -2),
+    (dict(pps=0), -2), (dict(max_k=512 * 16 + 1), -2),
+    # one sequence's q rows beyond 2^31 - 1 bytes
+    (dict(max_q=262000, max_k=262000, pps=16384, n_seqs=1), -2),
+    (dict(d=128), -3), (dict(hq=64, hkv=2), -3),
+    (dict(scale=0.0), -4), (dict(scale=float("inf")), -4),
+    (dict(q=FAKE + 8), -5), (dict(vc=FAKE + 4), -5), (dict(out=FAKE + 2), -5), (dict(cu=FAKE + 2), -5),
+    (dict(lens=FAKE + 1), -5),
+])
+def test_prefill_kvcache_host_validation_codes(kw, code):
+    assert pcall(**kw) == code
+
+
+def test_prefill_kvcache_validation_precedes_device_check():
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert pcall() == -6
+    assert pcall(n_seqs=0, max_q=0, max_k=0) == -6
+    assert pcall(window=128, sinks=FAKE) == -6

@@ -72,10 +72,10 @@ def test_decode_small_parity(case, oracle_lib):
     assert np.all(got[empty] == 0.0), "a sequence without keys must give zero rows"
 
 
-@pytest.mark.parametrize("name", list(workloads.CACHE_WORKLOADS))
+@pytest.mark.parametrize("name", list(workloads.DECODE_WORKLOADS))
 def test_decode_workload_parity(name, oracle_lib):
     """Every output element of the benchmark's decode workloads, same launch as the benchmark."""
-    wl = workloads.CACHE_WORKLOADS[name]
+    wl = workloads.DECODE_WORKLOADS[name]
     inp = workloads.make_cache_inputs(wl)
     say(f"decode workload parity {name}")
     got = f64(run_gpu_decode(inp).cpu())
