@@ -8,7 +8,12 @@
 One step is one ts_mha_prefill call over the whole workload: every stage of the
 operation (tile walk, QK^T, mask, online softmax with sink, PV, epilogue) runs
 inside that single kernel launch.  Inputs are seeded synthetic tensors already
-resident in device memory when the timed region starts.
+resident in device memory when the timed region starts.  Warm-up runs at least
+--warmup launches and at least --warmup-seconds (default 1 s) of them: under a
+sudden load the GPU's clocks take tens of milliseconds to settle, and launches
+in that ramp run up to 25% slower than in steady state.
+
+    python bench.py --trace-summary DIR --steps K   # durations from a rocprofv3 kernel trace
 
 Metric: FLOP = 4 * head_dim * n_q_heads * (visible query-key pairs per head),
 i.e. 2*head_dim flops for q.k and 2*head_dim for the weighted sum of v, counted
@@ -150,11 +155,40 @@ def cpu_baseline(wl, inp, target_s: float):
                       f"fp64 oracle rows; {dt:.1f} s wall"}
 
 
+def trace_summary(root: str, last: int):
+    """Per-kernel durations from rocprofv3's kernel_trace.csv files under root: every dispatch,
+    and the last `last` prefill dispatches (the timed region of a bench.py run)."""
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),
+                             r["Kernel_Name"]))
+    rows.sort()
+    names = sorted({n for _, _, n in rows})
+    print(f"{'kernel':70s} {'calls':>6s} {'avg_ns':>12s} {'min_ns':>10s} {'max_ns':>10s}")
+    for n in names:
+        d = [x for _, x, k in rows if k == n]
+        print(f"{n[:70]:70s} {len(d):6d} {sum(d) / len(d):12.1f} {min(d):10d} {max(d):10d}")
+    d = [x for _, x, k in rows if "prefill_fwd" in k][-last:]
+    if d:
+        print(f"timed region (last {len(d)} prefill dispatches): avg_ns {sum(d) / len(d):.1f} "
+              f"min_ns {min(d)} max_ns {max(d)}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
+                    help="keep warming up until this much time has passed as well (the GPU's "
+                         "clocks take tens of milliseconds of load to reach their steady state)")
+    ap.add_argument("--trace-summary", default=None, metavar="DIR",
+                    help="summarise the prefill dispatches of a rocprofv3 kernel trace under DIR "
+                         "(the last --steps of them: the timed region) and exit")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -167,6 +201,9 @@ def main():
     ap.add_argument("--prefill-kvcache", action="store_true",
                     help="time prefill of new rows against a paged KV cache instead")
     a = ap.parse_args()
+    if a.trace_summary:
+        trace_summary(a.trace_summary, a.steps)
+        return
     if a.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {a.gpus} is not supported "
               "(the operation shards by KV-head group or by sequence with no exchange, "
@@ -180,6 +217,17 @@ def main():
 
     dev = torch.device("cuda", 0)
     stream = torch.cuda.current_stream(dev)
+    warm_counts = {}
+
+    def warm(fn) -> int:
+        """At least --warmup launches and at least --warmup-seconds of them; returns the count."""
+        n, t = 0, time.perf_counter()
+        while n < a.warmup or time.perf_counter() - t < a.warmup_seconds:
+            for _ in range(25):
+                fn()
+            n += 25
+            torch.cuda.synchronize()
+        return n
 
     def timed(wl, steps, warmup, copy_calibration=False):
         """Resident inputs, W warm-up launches, then K launches timed on the host clock and by
@@ -201,8 +249,7 @@ def main():
                 dst.copy_(src)
             torch.cuda.synchronize()
             del src, dst
-        for _ in range(warmup):
-            step()
+        warm_counts[wl.name] = warm(step)
         # One event pair on the launch stream around the K back-to-back launches:
         # the GPU-side span divided by K is the kernel's average launch duration
         # (events between launches would add their own dispatch gaps).
@@ -234,8 +281,7 @@ def main():
                                                max_seqlen_q=wl.max_seqlen_q,
                                                max_seqlen_k=wl.max_seqlen_k, stream=stream)
 
-            for _ in range(a.warmup):
-                pstep()
+            warm(pstep)
             ev0 = torch.cuda.Event(enable_timing=True)
             ev1 = torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
@@ -276,8 +322,7 @@ def main():
                                               max_seqlen_k=wl.max_seqlen_k, workspace=ws,
                                               stream=stream)
 
-            for _ in range(a.warmup):
-                dstep()
+            warm(dstep)
             ev0 = torch.cuda.Event(enable_timing=True)
             ev1 = torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
@@ -351,6 +396,7 @@ def main():
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
+        "warmup_launches": warm_counts[name],
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -38,21 +38,18 @@
 // lands in the XOR-swizzled layout the readers expect.  The XOR pattern is laid
 // out for an LDS that serves 256 bytes (64 banks) per cycle.
 //
-// Softmax.  Base 2 throughout: t = s * scale * log2(e).  A row's result does
-// not depend on the reference m its probabilities exp2(t - m) are measured
-// against, as long as nothing leaves fp32 range.  The tiles are walked from
-// the last to the first: the diagonal tiles (those holding the work-group's
-// own positions) come first and run a streaming softmax with running maxima
-// and fp32 row sums (tile_exact), which leaves every row a reference that is
-// a maximum of its real logits (and of the sink).  The remaining tiles keep
-// that reference fixed: the row's running maximum is at least as large, so
-// probabilities are never smaller than under a streaming softmax and no
-// rescaling is needed; there is no per-element maximum.  Their row sums
-// accumulate on the matrix pipe (see row_sums), so the per-element vector
-// work is one fma, one exp2 and half a bf16 pack.  If a row's logits climb so
-// far above its reference that a sum passes 2^64 or a value stops being
-// finite, the work-group redoes its rows with tile_exact throughout.  The
-// sink's own term exp2(sigma - m) joins the denominator at the end.
+// Softmax.  Base 2 throughout: t = s * scale * log2(e).  The query operand
+// is q * scale * log2(e) rounded once to bf16, so the score accumulators hold
+// t itself.  A row's result does not depend on the reference m its
+// probabilities exp2(t - m) are measured against, as long as nothing leaves
+// fp32 range; the fast pass takes m = 0 for every row, so a probability is
+// exp2 of its score accumulator: no running maximum, no rescaling, and the
+// per-element vector work is one exp2 and half a bf16 pack.  Row sums
+// accumulate on the matrix pipe (see row_sums).  If a row's sum leaves
+// [2^-64, 2^64] or a value stops being finite (logits beyond about +-64 in
+// base 2), the work-group redoes its rows with tile_exact, a streaming
+// softmax with running maxima.  The sink's own term exp2(sigma - m) joins the
+// denominator at the end.
 //
 // Scheduling.  Each tile runs in six steps over its four 32 x 32 score
 // blocks; the softmax of one block is interleaved instruction by instruction
@@ -85,7 +82,7 @@ constexpr int kRowBytes = kD * 2;             // one K or V row in bytes
 constexpr int kChunks = kRowBytes / 16;       // 16-byte chunks per row
 constexpr int kTileChunks = kBK * kChunks;    // 16-byte chunks per tile
 constexpr int kTileBytes = kTileChunks * 16;
-constexpr float kFastSumLimit = 1.8446744e19f;  // 2^64: largest row sum the fast pass keeps
+constexpr float kFastSumLimit = 1.8446744e19f;  // 2^64: the fast pass keeps row sums in [2^-64, 2^64]
 constexpr int kSlots = 2;                     // LDS buffers for K and for V tiles
 
 
@@ -245,25 +242,35 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
       }
     }
   };
-  // Tiles are walked from the last (the diagonal) back to the first.  The
-  // first tile's loads go out before the query loads below, so the two
-  // latencies overlap.
-  issue_tile(kt1, 0);
-
-
   // ---- this lane's two query rows (one per 32-column block nb).  Lane l holds
   // head_dim elements 16 ks + 8 hi .. + 7 of its row for ks = 0..3.
   int pos[2], head[2];
   bf16x8 qf[2][4];
   float mref[2], lsum[2];
   f32x16 o[2][2];  // [d block][nb]: O^T, rows = head_dim, columns = queries
-  float sink_t[2];  // the sink logit times log2 e (-inf without sinks)
+  // The sink logits are loaded here, without a branch (a descriptor of range
+  // 0 when there are no sinks reads zeros), and first used in the epilogue:
+  // the compiler does not see the inline-assembly loads below, so the wait it
+  // places before a use of its own load also waits for them; a use in the
+  // prologue would hold back the query loads until the first tile landed.
+  const __amdgpu_buffer_rsrc_t rsink =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.sinks, 0, p.sinks ? Hq * 4 : 0, kBufferConfig);
+  float sink_raw[2];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int r = 64 * w + 32 * nb + l32;
     head[nb] = g * G + r % G;
     pos[nb] = p0 + r / G;
-    sink_t[nb] = p.sinks ? p.sinks[head[nb]] * kLog2e : -INFINITY;
+    sink_raw[nb] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsink, head[nb] * 4, 0, 0));
+  }
+  // the sink logit in base 2 (-inf without sinks)
+  auto sink_t = [&](int nb) { return p.sinks ? sink_raw[nb] * kLog2e : -INFINITY; };
+
+  // The first tile's page id is looked up before any inline-assembly load is
+  // in flight (the compiler's wait for it would wait for those too).
+  if constexpr (PAGED) {
+    (void)tile_page(kt1);
+    asm volatile("" : : "v"(pgv));  // the wait for the ids stays ahead of those loads
   }
   // The query rows go through LDS with the same wave-wide loads as K and V:
   // each 1 KiB load covers 8 whole rows (the G heads of a position are
@@ -281,15 +288,23 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
       lds_dma16(lds_q_base + it * 1024, rq, ((p0 + r / G) * Hq + g * G + r % G) * kRowBytes + data_ch * 16);
     }
   }
-  wait_vmem<0>();  // the query rows (and the first tile) have landed in LDS
-  // The first tile's loads and the query loads complete here, not inside the
-  // tile loop.
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  // Tiles are walked from the last (the diagonal) back to the first.  The
+  // first tile's loads follow the query loads, so the two latencies overlap
+  // and the query rows, which land first, are converted while the tile is
+  // still in flight.
+  issue_tile(kt1, 0);
+  wait_vmem<4>();  // the query rows have landed (loads complete in order; the tile's 4 may not)
+  // The query operand carries the softmax scale and log2 e, rounded once to
+  // bf16 (qf = q * c): the score accumulators then hold base-2 logits and the
+  // probabilities need no multiply.
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      qf[nb][ks] = __builtin_bit_cast(bf16x8, lds_q[w * 64 * kChunks + swz(32 * nb + l32, 2 * ks + hi)]);
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 x = __builtin_bit_cast(bf16x8, lds_q[w * 64 * kChunks + swz(32 * nb + l32, 2 * ks + hi)]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[nb][ks][e] = (__bf16)((float)x[e] * c);
+    }
 
   // K fragments (A operand) of key half mb for the four 16-wide steps of head_dim.
   // Per-lane byte offsets of the operand reads within a tile, fixed for the
@@ -354,16 +369,17 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float pe = __builtin_amdgcn_exp2f(fmaf(sc[e], c, -m));
+      const float pe = __builtin_amdgcn_exp2f(sc[e] - m);
       if (e < 8) plo[e] = (__bf16)pe; else phi[e - 8] = (__bf16)pe;
       if (e & 1) a1 += pe; else a0 += pe;
     }
     return a0 + a1;
   };
-  auto block_probs_nosum = [&](const f32x16& sc, float m, bf16x8& plo, bf16x8& phi) {
+  // Probabilities of the fast pass: against reference 1, exp2 of the score itself.
+  auto block_probs_fast = [&](const f32x16& sc, bf16x8& plo, bf16x8& phi) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float pe = __builtin_amdgcn_exp2f(fmaf(sc[e], c, -m));
+      const float pe = __builtin_amdgcn_exp2f(sc[e]);
       if (e < 8) plo[e] = (__bf16)pe; else phi[e - 8] = (__bf16)pe;
     }
   };
@@ -412,6 +428,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   using I4 = std::integral_constant<int, 4>;
   using I6 = std::integral_constant<int, 6>;
   auto tile_fast = [&](auto masked_tag, const u32x4* kl, lds_char* vb, int k0) {
+    constexpr int nv = 6;  // vector instructions after each score MFMA
+    constexpr int nw = 4;  // ... after each PV or row-sum MFMA
     bf16x8 ka[4], kb[4], pf[4][2], va[2][2], vc[2][2];
     read_k(kl, 0, ka);
     read_k(kl, 1, kb);
@@ -421,24 +439,24 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
     read_v(vb, 0, va[0]);
     read_v(vb, 1, va[1]);
     const f32x16 s10 = qk(masked_tag, kb, 1, 0, k0);
-    block_probs_nosum(s00, mref[0], pf[0][0], pf[1][0]);
-    interleave(I4{}, std::integral_constant<int, 10>{});
+    block_probs_fast(s00, pf[0][0], pf[1][0]);
+    interleave(I4{}, std::integral_constant<int, nv>{});
     __builtin_amdgcn_sched_barrier(0);
     const f32x16 s11 = qk(masked_tag, kb, 1, 1, k0);
-    block_probs_nosum(s01, mref[1], pf[0][1], pf[1][1]);
-    interleave(I4{}, std::integral_constant<int, 10>{});
+    block_probs_fast(s01, pf[0][1], pf[1][1]);
+    interleave(I4{}, std::integral_constant<int, nv>{});
     __builtin_amdgcn_sched_barrier(0);
     read_v(vb, 2, vc[0]);
     read_v(vb, 3, vc[1]);
     pv(va, pf, 0, 0);
     row_sums(pf, 0, 0);
-    block_probs_nosum(s10, mref[0], pf[2][0], pf[3][0]);
-    interleave(I6{}, std::integral_constant<int, 7>{});
+    block_probs_fast(s10, pf[2][0], pf[3][0]);
+    interleave(I6{}, std::integral_constant<int, nw>{});
     __builtin_amdgcn_sched_barrier(0);
     pv(va, pf, 0, 1);
     row_sums(pf, 0, 1);
-    block_probs_nosum(s11, mref[1], pf[2][1], pf[3][1]);
-    interleave(I6{}, std::integral_constant<int, 7>{});
+    block_probs_fast(s11, pf[2][1], pf[3][1]);
+    interleave(I6{}, std::integral_constant<int, nw>{});
     __builtin_amdgcn_sched_barrier(0);
     pv(vc, pf, 1, 0);
     row_sums(pf, 1, 0);
@@ -447,11 +465,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   };
 
   // ---- exact tile: streaming softmax with running maxima and fp32 row sums
-  // on the vector ALU.  It runs the diagonal tiles, which come first in the
-  // walk, and so sets each row's reference to a maximum of real logits; and
-  // it runs every tile when the fast pass of a work-group overflowed.  Each
-  // key half raises the row maxima, rescales the accumulators, then adds its
-  // probabilities.
+  // on the vector ALU.  It runs every tile of a work-group whose fast pass
+  // left range.  Each key half raises the row maxima, rescales the
+  // accumulators, then adds its probabilities.
   auto tile_exact = [&](auto masked_tag, const u32x4* kl, lds_char* vb, int k0) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -460,7 +476,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         const f32x16 sc = qk(masked_tag, ka, mb, nb, k0);
-        const float mx = pair_max(max16(sc)) * c;
+        const float mx = pair_max(max16(sc));
         if (mx > mref[nb]) {
           const float alpha = __builtin_amdgcn_exp2f(mref[nb] - mx);
           lsum[nb] *= alpha;
@@ -485,27 +501,27 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   // [ktB, kt1] hold keys past some row's position (they also hold every row's
   // own key), tiles [kt0, ktA) may hold keys that left some row's window.
   //   unmasked <=> k0 + kBK - 1 <= p0  and (no window or (p0 + P - 1) - k0 < window)
-  // The diagonal tiles run exactly (running maxima); after them each row's
-  // reference stays fixed, a maximum the row's running maximum reaches, so
-  // the remaining probabilities are never below their streaming-softmax
-  // values.  The runs are separate loops so that each loop body holds one
-  // kind of tile.
+  // The runs are separate loops so that each loop body holds one kind of
+  // tile.
   const int ktB = max(kt0, min(kt1 + 1, (qoff + p0 + 1) / kBK));  // first tile with k0 + kBK - 1 > qoff + p0
   const int xa = qoff + p0 + P - p.window;  // first tile with k0 >= xa: all its keys inside every window
   const int ktA = (WINDOWED && xa > 0) ? min(ktB, max(kt0, (xa + kBK - 1) / kBK)) : kt0;
-  auto walk = [&](auto tile_fn, auto masked_tag, int kt_hi, int kt_lo) {
+  auto walk = [&](auto tile_fn, int kt_hi, int kt_lo) {
     for (int kt = kt_hi; kt >= kt_lo; --kt) {
       const int buf = (kt1 - kt) & 1;
       wait_vmem<0>();   // this wave's loads of tile kt have landed
       __syncthreads();  // every wave's have; the previous tile is fully consumed
       if (kt > kt0) issue_tile(kt - 1, buf ^ 1);
-      tile_fn(masked_tag, &lds_k[buf * kTileChunks], (lds_char*)&lds_v[buf * kTileChunks], kt * kBK);
+      tile_fn(&lds_k[buf * kTileChunks], (lds_char*)&lds_v[buf * kTileChunks], kt * kBK);
     }
   };
+  auto exact_masked = [&](const u32x4* kl, lds_char* vb, int k0) { tile_exact(std::true_type{}, kl, vb, k0); };
+  auto fast_masked = [&](const u32x4* kl, lds_char* vb, int k0) { tile_fast(std::true_type{}, kl, vb, k0); };
+  auto fast_open = [&](const u32x4* kl, lds_char* vb, int k0) { tile_fast(std::false_type{}, kl, vb, k0); };
   auto reset = [&]() {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      mref[nb] = sink_t[nb];
+      mref[nb] = sink_t(nb);
       lsum[nb] = 0.f;
       lacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -516,23 +532,22 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   };
 
   reset();
+  mref[0] = mref[1] = 0.f;  // the fast pass measures every probability against 1
   __builtin_amdgcn_s_setprio(0);
-  walk(tile_exact, std::true_type{}, kt1, ktB);
-  walk(tile_fast, std::false_type{}, ktB - 1, ktA);
-  if constexpr (WINDOWED) walk(tile_fast, std::true_type{}, ktA - 1, kt0);
-  // A row's sum: its diagonal tiles' fp32 sums (split over the lane pair) plus
-  // the row-sum accumulators of the other tiles, where query q of block nb
-  // sits in lane q % 16, element q / 16.
+  walk(fast_masked, kt1, ktB);
+  walk(fast_open, ktB - 1, ktA);
+  if constexpr (WINDOWED) walk(fast_masked, ktA - 1, kt0);
+  // A row's sum from the row-sum accumulators: query q of block nb sits in
+  // lane q % 16, element q / 16.
   float lrow[2];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const float e0 = __shfl(lacc[nb][0], l32 & 15);
     const float e1 = __shfl(lacc[nb][1], l32 & 15);
-    lrow[nb] = pair_sum(lsum[nb]) + ((l32 < 16) ? e0 : e1);
+    lrow[nb] = (l32 < 16) ? e0 : e1;
   }
-  // The fast pass is kept unless some row's probabilities grew so far past its
-  // reference that the sums lost range: a row sum above 2^64, or a sum or an
-  // output that is not finite.  Then the work-group redoes its rows exactly.
+  // The fast pass is kept unless a row's sum left [2^-64, 2^64] or a sum or
+  // an output is not finite.  Then the work-group redoes its rows exactly.
   {
     bool bad = false;
 #pragma unroll
@@ -542,7 +557,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
       for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) osum += o[db][nb][e];
-      bad = bad || !(lrow[nb] <= kFastSumLimit) || !(fabsf(osum) <= 3.0e38f);
+      bad = bad || !(lrow[nb] <= kFastSumLimit) || !(lrow[nb] >= 1.f / kFastSumLimit) ||
+            !(fabsf(osum) <= 3.0e38f);
     }
     const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
     if (lane == 0) redo_vote[w] = wave_bad ? 1 : 0;
@@ -551,7 +567,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
     if (redo) {
       reset();
       issue_tile(kt1, 0);
-      walk(tile_exact, std::true_type{}, kt1, kt0);
+      walk(exact_masked, kt1, kt0);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) lrow[nb] = pair_sum(lsum[nb]);
     }
@@ -561,7 +577,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     float lt = lrow[nb];
-    if (p.sinks) lt += __builtin_amdgcn_exp2f(sink_t[nb] - mref[nb]);
+    if (p.sinks) lt += __builtin_amdgcn_exp2f(sink_t(nb) - mref[nb]);
     const float inv = 1.f / lt;
     if (pos[nb] < L) {
       uint16_t* orow = p.out + ((int64_t)(s + pos[nb]) * Hq + head[nb]) * kD;

@@ -49,6 +49,45 @@ def say(msg: str):
     print(f"[gpu-case] {msg}", flush=True)
 
 
+LN2 = 0.6931471805599453
+
+
+def base2_inputs(inp: dict) -> dict:
+    """The attention the prefill kernels evaluate, as oracle inputs.
+
+    The prefill kernels fold softmax_scale * log2(e) into their query operand:
+    q~ = bf16(fp32(q) * c) with c = fp32(scale * log2 e), each step rounded to
+    nearest even, and take exp2 of q~.k.  exp2(q~.k) is exp(ln2 * q~.k), so the
+    oracle run on q~ with scale ln 2 (sinks unchanged: they stay natural-log
+    logits) is exactly that attention; what remains between it and the kernel
+    are the roundings rounding_bound covers.  Works on packed (make_inputs) and
+    cache (make_cache_inputs) input dicts.
+    """
+    scale = float(np.float32(inp["softmax_scale"]))
+    c = np.float32(scale * 1.4426950408889634)
+    qt = (inp["q"].to(torch.float32) * torch.tensor(c, dtype=torch.float32)).to(torch.bfloat16)
+    return dict(inp, q=qt, softmax_scale=LN2)
+
+
+GATE_MAX, GATE_MEAN = 2e-2, 2e-3
+
+
+def assert_within_rounding(got, inp: dict, lib=None, gate: bool = True, what: str = ""):
+    """got (fp64) within rounding_bound of the oracle on the attention the kernel
+    evaluates (base2_inputs); with gate, also within the parity gate (max |err| <=
+    2e-2, mean <= 2e-3) of the oracle on the original inputs."""
+    from oracle import oracle
+    b2 = base2_inputs(inp)
+    ref2 = oracle.prefill(*oracle_args(b2), lib=lib)
+    excess = np.abs(got - ref2) - rounding_bound(b2, ref2, lib)
+    assert excess.max() <= 0, f"{what}: rounding bound exceeded by {excess.max():.3e}"
+    if gate:
+        ref = oracle.prefill(*oracle_args(inp), lib=lib)
+        d = np.abs(got - ref)
+        assert d.max() <= GATE_MAX and d.mean() <= GATE_MEAN, \
+            f"{what}: gate max {d.max():.3e} mean {d.mean():.3e}"
+
+
 def rounding_bound(inp: dict, ref, lib=None):
     """Elementwise error allowance of a bf16-P, fp32-accumulate, bf16-output kernel.
 

@@ -15,7 +15,7 @@ import torch
 import sinks_ts_mha_amd as tm
 from oracle import oracle
 from sinks_ts_mha_amd import workloads
-from _util import f64, oracle_args, rounding_bound, run_gpu, say
+from _util import assert_within_rounding, f64, oracle_args, run_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -94,8 +94,7 @@ def test_window_edges_tight(window, oracle_lib):
     inp = workloads.make_inputs(wl)
     say(f"window edge W={window}")
     got = f64(run_gpu(inp).cpu())
-    ref = oracle.prefill(*oracle_args(inp), lib=oracle_lib)
-    assert np.all(np.abs(got - ref) <= rounding_bound(inp, ref, oracle_lib))
+    assert_within_rounding(got, inp, oracle_lib)
 
 
 @pytest.mark.parametrize("sink", [None, 0.0, 4.0, 80.0, -80.0])
@@ -105,8 +104,7 @@ def test_sink_values(sink, oracle_lib):
     inp["sinks"] = None if sink is None else torch.full((16,), sink)
     say(f"sink value {sink}")
     got = f64(run_gpu(inp).cpu())
-    ref = oracle.prefill(*oracle_args(inp), lib=oracle_lib)
-    assert np.all(np.abs(got - ref) <= rounding_bound(inp, ref, oracle_lib))
+    assert_within_rounding(got, inp, oracle_lib)
     if sink == 80.0:
         assert np.max(np.abs(got)) < 1e-6
 
@@ -125,9 +123,11 @@ def test_wide_logit_range(window, with_sinks, oracle_lib):
         inp["sinks"] = None
     say(f"wide logit range window={window} sinks={with_sinks}")
     got = f64(run_gpu(inp).cpu())
-    ref = oracle.prefill(*oracle_args(inp), lib=oracle_lib)
     assert np.all(np.isfinite(got))
-    assert np.all(np.abs(got - ref) <= rounding_bound(inp, ref, oracle_lib))
+    # Logits this spread make the query operand's rounding (relative 2^-8) move
+    # near-tied probabilities far more than the gate allows, so only the
+    # elementwise bound against the attention the kernel evaluates applies.
+    assert_within_rounding(got, inp, oracle_lib, gate=False)
 
 
 def test_edge_shapes(oracle_lib):
@@ -138,8 +138,7 @@ def test_edge_shapes(oracle_lib):
         got = run_gpu(inp)
         torch.cuda.synchronize()
         if wl.total_tokens:
-            ref = oracle.prefill(*oracle_args(inp), lib=oracle_lib)
-            assert np.all(np.abs(f64(got.cpu()) - ref) <= rounding_bound(inp, ref, oracle_lib))
+            assert_within_rounding(f64(got.cpu()), inp, oracle_lib)
 
 
 def test_no_sequences_is_noop():
@@ -214,8 +213,7 @@ def test_runs_on_a_side_stream(oracle_lib):
     with torch.cuda.stream(s):
         got = run_gpu(inp, stream=s)
     s.synchronize()
-    ref = oracle.prefill(*oracle_args(inp), lib=oracle_lib)
-    assert np.all(np.abs(f64(got.cpu()) - ref) <= rounding_bound(inp, ref, oracle_lib))
+    assert_within_rounding(f64(got.cpu()), inp, oracle_lib)
 
 
 def test_arch_check_hook(monkeypatch):
