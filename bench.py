@@ -178,6 +178,23 @@ def trace_summary(root: str, last: int):
               f"min_ns {min(d)} max_ns {max(d)}")
 
 
+def counter_summary(root: str):
+    """Average value per dispatch of each counter, per kernel and grid size, in rocprofv3's
+    counter_collection.csv files under root."""
+    import csv
+    import glob
+    acc = {}
+    for path in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                key = (r["Kernel_Name"], int(r["Grid_Size"]), r["Counter_Name"])
+                d = acc.setdefault(key, {})
+                d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    print(f"{'kernel':64s} {'grid':>8s} {'counter':12s} {'dispatches':>10s} {'avg_per_dispatch':>17s}")
+    for (k, g, c), d in sorted(acc.items()):
+        print(f"{k[:64]:64s} {g:8d} {c:12s} {len(d):10d} {sum(d.values()) / len(d):17.3f}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,6 +203,8 @@ def main():
     ap.add_argument("--warmup-seconds", type=float, default=1.0,
                     help="keep warming up until this much time has passed as well (the GPU's "
                          "clocks take tens of milliseconds of load to reach their steady state)")
+    ap.add_argument("--counter-summary", default=None, metavar="DIR",
+                    help="average per dispatch of each counter of a rocprofv3 --pmc run under DIR, and exit")
     ap.add_argument("--trace-summary", default=None, metavar="DIR",
                     help="summarise the prefill dispatches of a rocprofv3 kernel trace under DIR "
                          "(the last --steps of them: the timed region) and exit")
@@ -203,6 +222,9 @@ def main():
     a = ap.parse_args()
     if a.trace_summary:
         trace_summary(a.trace_summary, a.steps)
+        return
+    if a.counter_summary:
+        counter_summary(a.counter_summary)
         return
     if a.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {a.gpus} is not supported "
@@ -281,7 +303,7 @@ def main():
                                                max_seqlen_q=wl.max_seqlen_q,
                                                max_seqlen_k=wl.max_seqlen_k, stream=stream)
 
-            warm(pstep)
+            n_warm = warm(pstep)
             ev0 = torch.cuda.Event(enable_timing=True)
             ev1 = torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
@@ -300,7 +322,8 @@ def main():
                               "value": round(flops / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
                               "kernel_avg_us": round(ms_gpu * 1e3, 2),
                               "frac": round(flops / (ms_gpu * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                              "flops": flops, "steps": a.steps, "warmup": a.warmup}), flush=True)
+                              "flops": flops, "steps": a.steps, "warmup": a.warmup,
+                              "warmup_launches": n_warm}), flush=True)
             del q, kc, vc, sinks, cuq, lens, table, out
             torch.cuda.empty_cache()
         return
@@ -376,7 +399,8 @@ def main():
                               "value": round(flops / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
                               "kernel_avg_us": round(ms_kernel * 1e3, 2),
                               "frac": round(flops / (ms_kernel * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                              "steps": a.steps, "warmup": a.warmup}), flush=True)
+                              "steps": a.steps, "warmup": a.warmup,
+                              "warmup_launches": warm_counts[wl.name]}), flush=True)
             torch.cuda.empty_cache()
         return
 
