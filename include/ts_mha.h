@@ -53,10 +53,11 @@ extern "C" {
 #define TS_MHA_ERR_NULL_ARG (-1)     /* a required pointer is NULL */
 #define TS_MHA_ERR_BAD_SHAPE (-2)    /* heads <= 0, n_q_heads % n_kv_heads != 0, n_seqs < 0,
                                         max_seqlen < 0, the launch grid would overflow, or one
-                                        sequence's q rows ((max_seqlen + 256) * n_q_heads * 128
-                                        bytes) or k/v rows ((max_seqlen + 64) * n_kv_heads * 128
-                                        bytes) would exceed 2^31 - 1 bytes */
-#define TS_MHA_ERR_UNSUPPORTED (-3)  /* head_dim != 64, or n_q_heads / n_kv_heads not in {1,2,4,8,16} */
+                                        sequence's q rows ((max_seqlen + 256) * n_q_heads * 2 *
+                                        head_dim bytes) or k/v rows ((max_seqlen + 64) *
+                                        n_kv_heads * 2 * head_dim bytes) would exceed 2^31 - 1 */
+#define TS_MHA_ERR_UNSUPPORTED (-3)  /* head_dim not 64 (ts_mha_prefill: 64 or 128), or
+                                        n_q_heads / n_kv_heads not in {1,2,4,8,16} */
 #define TS_MHA_ERR_BAD_SCALE (-4)    /* softmax_scale not finite or <= 0 */
 #define TS_MHA_ERR_ALIGN (-5)        /* q, k, v or out not 16-byte aligned; sinks or cu_seqlens not 4-byte aligned */
 #define TS_MHA_ERR_NO_DEVICE (-6)    /* no HIP device is present */
@@ -80,7 +81,9 @@ extern "C" {
  *               cu_seqlens[n_seqs] = T.  Empty sequences are allowed.
  *  n_q_heads, n_kv_heads   > 0, n_q_heads a multiple of n_kv_heads with
  *               group size n_q_heads / n_kv_heads in {1, 2, 4, 8, 16}
- *  head_dim     must be 64
+ *  head_dim     64 or 128 (the head widths of the kernel traits in the
+ *               TokenSpeed-kernel README, "Public API"); q, k, v and out rows
+ *               hold head_dim elements
  *  window       <= 0: full causal; > 0: key j visible to query i iff 0 <= i - j < window
  *  softmax_scale  finite, > 0; applied to q.k exactly as given
  *  out          device, bf16 [T][n_q_heads][head_dim], 16-byte aligned; every

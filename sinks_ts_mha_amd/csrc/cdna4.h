@@ -65,6 +65,20 @@ __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
+// Range tests on the bits of an fp32 value.  The kernels are compiled with
+// -fno-honor-nans, under which the compiler may fold !(x <= c) into x > c,
+// a test that a NaN passes; integer tests on the exponent field are exact.
+// finite_bits: x is neither infinite nor NaN.
+__device__ __forceinline__ bool finite_bits(float x) {
+  return (__float_as_uint(x) & 0x7f800000u) != 0x7f800000u;
+}
+// positive_in_binade_range: x > 0 with 2^lo <= x < 2^(hi + 1) (false for NaN,
+// infinities, zeros, denormals and negative values).
+__device__ __forceinline__ bool positive_in_binade_range(float x, int lo, int hi) {
+  const int e = (int)(__float_as_uint(x) >> 23) - 127;  // a set sign bit makes e >= 129
+  return e >= lo && e <= hi;
+}
+
 // Position of 16-byte chunk `ch` of row `row` (8 chunks of a 128-byte row) in
 // an LDS tile.  The LDS serves 64 banks of 4 bytes per cycle, two 128-byte
 // rows; the XOR key (row bit 1 as chunk bit 2, row bits 2..3 as chunk bits

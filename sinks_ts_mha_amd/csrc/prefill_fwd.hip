@@ -46,7 +46,7 @@
 // exp2 of its score accumulator: no running maximum, no rescaling, and the
 // per-element vector work is one exp2 and half a bf16 pack.  Row sums
 // accumulate on the matrix pipe (see row_sums).  If a row's sum leaves
-// [2^-64, 2^64] or a value stops being finite (logits beyond about +-64 in
+// [2^-64, 2^65) or a value stops being finite (logits beyond about +-64 in
 // base 2), the work-group redoes its rows with tile_exact, a streaming
 // softmax with running maxima.  The sink's own term exp2(sigma - m) joins the
 // denominator at the end.
@@ -82,7 +82,7 @@ constexpr int kRowBytes = kD * 2;             // one K or V row in bytes
 constexpr int kChunks = kRowBytes / 16;       // 16-byte chunks per row
 constexpr int kTileChunks = kBK * kChunks;    // 16-byte chunks per tile
 constexpr int kTileBytes = kTileChunks * 16;
-constexpr float kFastSumLimit = 1.8446744e19f;  // 2^64: the fast pass keeps row sums in [2^-64, 2^64]
+constexpr int kFastSumBinades = 64;  // the fast pass keeps row sums in [2^-64, 2^65)
 constexpr int kSlots = 2;                     // LDS buffers for K and for V tiles
 
 
@@ -546,7 +546,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
     const float e1 = __shfl(lacc[nb][1], l32 & 15);
     lrow[nb] = (l32 < 16) ? e0 : e1;
   }
-  // The fast pass is kept unless a row's sum left [2^-64, 2^64] or a sum or
+  // The fast pass is kept unless a row's sum left [2^-64, 2^65) or a sum or
   // an output is not finite.  Then the work-group redoes its rows exactly.
   {
     bool bad = false;
@@ -557,8 +557,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
       for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) osum += o[db][nb][e];
-      bad = bad || !(lrow[nb] <= kFastSumLimit) || !(lrow[nb] >= 1.f / kFastSumLimit) ||
-            !(fabsf(osum) <= 3.0e38f);
+      bad = bad || !positive_in_binade_range(lrow[nb], -kFastSumBinades, kFastSumBinades) ||
+            !finite_bits(osum);
     }
     const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
     if (lane == 0) redo_vote[w] = wave_bad ? 1 : 0;

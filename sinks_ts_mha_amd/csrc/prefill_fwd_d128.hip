@@ -1,0 +1,484 @@
+// prefill_fwd_d128.hip -- gfx950 (CDNA4) kernels for causal grouped-query
+// prefill attention with sliding windows and attention sinks at head_dim 128.
+//
+// The same operation as the head_dim 64 kernels (the `mha_prefill` call of the
+// TokenSpeed-kernel README, section "Public API"; sinks and sliding windows as
+// for the GPT-OSS layers of "TokenSpeed-kernel multi-silicon", section
+// "Числа: Gluon на AMD MI355X"), for the other head width the README's kernel
+// traits name.  The design follows the head_dim 64 kernel, resized:
+//
+// Work decomposition.  One work-group (4 waves) owns 128 query rows: all G
+// query heads of one KV head for P = 128 / G consecutive positions of one
+// sequence; each wave holds 32 of them, so that the output (128 x 32 fp32)
+// and the query operand (32 x 128 bf16) take the registers the head_dim 64
+// kernel spends on 64 rows.  Every K/V tile staged in LDS serves the whole
+// head group.
+//
+// Orientation.  Scores are formed transposed, S^T = K Q^T, with
+// v_mfma_f32_32x32x16_bf16 (two 32-key blocks per 64-key tile, eight 16-wide
+// steps of head_dim); lane l holds query l % 32.  The output is accumulated
+// transposed too, O^T += V^T P^T (four 32-row blocks of head_dim), with V^T
+// read by ds_read_b64_tr_b16 from the row-major V tile and P^T taken straight
+// from the score accumulators.
+//
+// Staging.  K and V tiles (64 rows of 256 bytes) move from HBM to LDS with
+// buffer_load_dwordx4 ... lds, double-buffered; the query rows are staged once
+// in the second slot before the walk, so the work-group uses 64 KiB of LDS and
+// two fit on a compute unit.  A 16-byte chunk c of row r sits at position
+// c ^ (((r & 3) << 2) | ((r >> 2) & 3)): 16 consecutive rows reading one chunk
+// (K and Q operands) and 4 aligned rows reading two adjacent chunks (the
+// transposed V reads) each hit distinct banks of the 64-bank LDS.
+//
+// Softmax.  As at head_dim 64: base 2, scale * log2(e) folded into the bf16
+// query operand, every probability exp2 of its score against reference 1,
+// row sums on the matrix pipe, and a streaming softmax with running maxima for
+// a work-group whose sums leave [2^-64, 2^65).
+#include <math.h>
+
+#include <type_traits>
+
+#include "cdna4.h"
+#include "prefill_fwd.h"
+
+namespace tsmha {
+
+using namespace cdna4;
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kD = 128;                        // head_dim
+constexpr int kBK = 64;                        // keys per LDS tile
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kQW = 32;                        // query rows per wave
+constexpr int kRows = kQW * kWaves;            // (query head, position) rows per work-group
+constexpr int kRowBytes = kD * 2;              // one K, V or Q row in bytes
+constexpr int kChunks = kRowBytes / 16;        // 16-byte chunks per row
+constexpr int kTileBytes = kBK * kRowBytes;    // 16 KiB
+constexpr int kTileChunks = kTileBytes / 16;
+constexpr int kFastSumBinades = 64;  // the fast pass keeps row sums in [2^-64, 2^65)
+
+struct Params {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* sinks;
+  const int32_t* cu;
+  uint16_t* out;
+  int32_t n_kv_heads;
+  int32_t n_seqs;
+  int32_t n_pblocks;
+  int32_t window;
+  float c;  // softmax_scale * log2(e)
+};
+
+// Position of 16-byte chunk `ch` of row `row` in a tile of 256-byte rows.
+__device__ __forceinline__ int key16(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+__device__ __forceinline__ int pos16(int row, int ch) { return row * kChunks + (ch ^ key16(row)); }
+
+__device__ __forceinline__ float pair_max(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float max16(const f32x16& a) {
+  float x = fmaxf(fmaxf(a[0], a[1]), a[2]);
+  float y = fmaxf(fmaxf(a[3], a[4]), a[5]);
+  x = fmaxf(fmaxf(x, a[6]), a[7]);
+  y = fmaxf(fmaxf(y, a[8]), a[9]);
+  x = fmaxf(fmaxf(x, a[10]), a[11]);
+  y = fmaxf(fmaxf(y, a[12]), a[13]);
+  return fmaxf(fmaxf(x, a[14]), fmaxf(y, a[15]));
+}
+
+template <int G, bool WINDOWED>
+__global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
+  constexpr int P = kRows / G;  // positions per work-group
+  __shared__ u32x4 lds_k[2 * kTileChunks];
+  __shared__ u32x4 lds_v[2 * kTileChunks];
+  __shared__ int redo_vote[kWaves];
+
+  const int Hkv = p.n_kv_heads;
+  const int Hq = Hkv * G;
+  const int id = blockIdx.x;
+  // KV head fastest (each XCD's L2 serves a fixed set of heads), position
+  // blocks last-first (the longest causal work starts first).
+  const int g = id % Hkv;
+  const int rest = id / Hkv;
+  const int b = rest % p.n_seqs;
+  const int pblk = p.n_pblocks - 1 - rest / p.n_seqs;
+  const int s = p.cu[b];
+  const int L = p.cu[b + 1] - s;
+  const int p0 = pblk * P;
+  if (p0 >= L) return;
+
+  __builtin_amdgcn_s_setprio(2);  // the prologue at raised priority, the walk at normal
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int r16 = lane & 15;
+  const int half16 = (lane >> 4) & 1;
+  const float c = p.c;
+
+  const int last = min(L, p0 + P) - 1;
+  const int first = WINDOWED ? max(0, p0 - p.window + 1) : 0;
+  const int kt0 = first / kBK;
+  const int kt1 = last / kBK;
+
+  // ---- K/V staging: tile t lives in slot (kt1 - t) & 1.  Wave w fills rows
+  // 16 w .. 16 w + 15 of a tile with four wave-wide 1 KiB loads (4 rows each)
+  // per tensor; each lane fetches the data chunk that belongs at its
+  // swizzled LDS position.  Rows past the sequence end read as zeros.
+  const int64_t seq_elems = (int64_t)s * Hkv * kD;
+  const int nbytes = L * Hkv * kRowBytes;
+  const int tile_stride = kBK * Hkv * kRowBytes;
+  const i32x4 rk = buffer_rsrc(p.k + seq_elems, nbytes);
+  const i32x4 rv = buffer_rsrc(p.v + seq_elems, nbytes);
+  int voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * w + 4 * i + (lane >> 4);
+    voff[i] = (row * Hkv + g) * kRowBytes + ((lane & 15) ^ key16(row)) * 16;
+  }
+  const uint32_t lds_k_base = lds_addr(lds_k) + w * 16 * kRowBytes;
+  const uint32_t lds_v_base = lds_addr(lds_v) + w * 16 * kRowBytes;
+  auto issue_tile = [&](int t, int buf) {
+    const int off = t * tile_stride;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lds_dma16(lds_k_base + buf * kTileBytes + i * 1024, rk, off + voff[i]);
+      lds_dma16(lds_v_base + buf * kTileBytes + i * 1024, rv, off + voff[i]);
+    }
+  };
+
+  // ---- this lane's query row: 32 w + l32 of the work-group.
+  const int r_me = kQW * w + l32;
+  const int head = g * G + r_me % G;
+  const int pos = p0 + r_me / G;
+  // The sink logit: a branch-free buffer load (range 0 without sinks), first
+  // used in the epilogue, so no wait for it holds back the loads below.
+  const __amdgpu_buffer_rsrc_t rsink =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.sinks, 0, p.sinks ? Hq * 4 : 0, kBufferConfig);
+  const float sink_raw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsink, head * 4, 0, 0));
+  auto sink_t = [&]() { return p.sinks ? sink_raw * kLog2e : -INFINITY; };
+
+  // The query rows go through slot 1 of the tiles (waves 0 and 1 in the K
+  // slot, 2 and 3 in the V slot; 8 KiB each), with eight wave-wide loads of 4
+  // whole rows, then the first tile into slot 0.  Slot 1 receives its first
+  // tile only after the walk's first barrier, when every wave holds its
+  // query operand in registers.
+  const uint32_t q_lds = (w < 2 ? lds_addr(lds_k) : lds_addr(lds_v)) + kTileBytes + (w & 1) * kQW * kRowBytes;
+  {
+    const i32x4 rq = buffer_rsrc(p.q + (int64_t)s * Hq * kD, L * Hq * kRowBytes);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 4 * i + (lane >> 4);  // within the wave's 32 rows
+      const int r = kQW * w + row;
+      const int data_ch = (lane & 15) ^ key16(row);
+      lds_dma16(q_lds + i * 1024, rq, ((p0 + r / G) * Hq + g * G + r % G) * kRowBytes + data_ch * 16);
+    }
+  }
+  issue_tile(kt1, 0);
+  wait_vmem<8>();  // the query rows have landed (loads complete in order; the tile's 8 may not)
+  // Query operand (B of the score MFMA) for the eight 16-wide steps of
+  // head_dim: lane l holds elements 16 ks + 8 hi .. + 7 of its row, times
+  // scale * log2(e), rounded once to bf16.
+  bf16x8 qf[8];
+  {
+    const lds_char* qb = (w < 2 ? (const lds_char*)lds_k : (const lds_char*)lds_v) + kTileBytes + (w & 1) * kQW * kRowBytes;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 x = *(const bf16x8*)(qb + pos16(l32, 2 * ks + hi) * 16);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)((float)x[e] * c);
+    }
+  }
+
+  // Per-lane byte offsets of the operand reads within a tile, fixed for the
+  // walk: K rows 32 mb + l32 share their swizzle with row l32, and the V rows
+  // of PV step s4 with step 0, so the key half and the step add immediates.
+  uint32_t koff[8], vlo_off[4], vhi_off[4];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) koff[ks] = (uint32_t)(pos16(l32, 2 * ks + hi) * 16);
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int key_lo = 4 * hi + (r16 >> 2);
+    const int key_hi = key_lo + 8;
+    const int d = 32 * db + 16 * half16 + 4 * (r16 & 3);
+    vlo_off[db] = (uint32_t)(pos16(key_lo, d >> 3) * 16 + (d & 7) * 2);
+    vhi_off[db] = (uint32_t)(pos16(key_hi, d >> 3) * 16 + (d & 7) * 2);
+  }
+  auto read_k = [&](const lds_char* kl, int mb, bf16x8 (&ka)[8]) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) ka[ks] = *(const bf16x8*)(kl + mb * 32 * kRowBytes + koff[ks]);
+  };
+  // V^T fragment (A of the PV MFMA) of PV step s4 (keys 16 s4 .. +15) and head_dim block db.
+  auto read_v = [&](const lds_char* vb, int s4, int db) -> bf16x8 {
+    const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + s4 * 16 * kRowBytes + vlo_off[db]));
+    const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + s4 * 16 * kRowBytes + vhi_off[db]));
+    const u32x2 u0 = __builtin_bit_cast(u32x2, t0);
+    const u32x2 u1 = __builtin_bit_cast(u32x2, t1);
+    return __builtin_bit_cast(bf16x8, u32x4{u0[0], u0[1], u1[0], u1[1]});
+  };
+  // Scores of key half mb: element e holds key k0 + 32 mb + 8 (e / 4) + 4 hi + e % 4.
+  // Masked tiles start the accumulator from the mask (0 visible, -inf hidden).
+  auto qk = [&](auto masked_tag, const bf16x8 (&ka)[8], int mb, int k0) -> f32x16 {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    f32x16 acc = {};
+    if constexpr (MASKED) {
+      const int di = pos - k0 - 4 * hi;
+      const int dw = di - p.window;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int cc = 32 * mb + 8 * (e / 4) + (e % 4);
+        const bool vis = (cc <= di) && (!WINDOWED || cc > dw);
+        acc[e] = vis ? 0.f : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], acc, 0, 0, 0);
+    return acc;
+  };
+  // bf16 P^T of one score block in the PV B-operand order (plo: PV step 2 mb,
+  // phi: step 2 mb + 1), against reference m (the fast pass: m = 0).
+  auto probs = [&](const f32x16& sc, float m, bf16x8& plo, bf16x8& phi) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float pe = __builtin_amdgcn_exp2f(sc[e] - m);
+      if (e < 8) plo[e] = (__bf16)pe; else phi[e - 8] = (__bf16)pe;
+    }
+  };
+  auto probs_sum = [&](const f32x16& sc, float m, bf16x8& plo, bf16x8& phi) -> float {
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float pe = __builtin_amdgcn_exp2f(sc[e] - m);
+      if (e < 8) plo[e] = (__bf16)pe; else phi[e - 8] = (__bf16)pe;
+      if (e & 1) a1 += pe; else a0 += pe;
+    }
+    return a0 + a1;
+  };
+  // Row sums on the matrix pipe: a 16 x 16 x 32 MFMA with a 0/1 selector as A
+  // reads a P^T fragment (16 keys x 32 queries) as B; rows 0 and 1 of the
+  // result (lanes 0..15, elements 0 and 1) accumulate the sums of queries n
+  // and n + 16.
+  const int lsel = ((lane & 15) == 0 && ((lane >> 4) & 1) == 0) || ((lane & 15) == 1 && ((lane >> 4) & 1) == 1);
+  const bf16x8 sel = __builtin_bit_cast(bf16x8, lsel ? u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u}
+                                                     : u32x4{0u, 0u, 0u, 0u});
+  f32x16 o[4];  // O^T blocks: head_dim 32 db .. + 31 x the wave's 32 queries
+  f32x4 lacc;
+  float mref, lsum;
+  // V^T fragments of PV steps s0, s0 + 1 (all four head_dim blocks), and
+  // O^T += V^T P^T over them.
+  auto read_v2 = [&](const lds_char* vb, int s0, bf16x8 (&va)[2][4]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) va[j][db] = read_v(vb, s0 + j, db);
+  };
+  auto pv2 = [&](const bf16x8 (&va)[2][4], const bf16x8 (&pf)[4], int s0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j][db], pf[s0 + j], o[db], 0, 0, 0);
+  };
+  auto interleave = [](auto k_tag, auto n_tag) {
+    constexpr int k = decltype(k_tag)::value;
+    constexpr int n = decltype(n_tag)::value;
+#pragma unroll
+    for (int i = 0; i < k; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, n, 0);
+    }
+  };
+
+  // ---- fast tile: probabilities against reference 1, row sums on the matrix
+  // pipe.  Four steps: scores of key half 0; scores of half 1 | probabilities
+  // of half 0; PV of half 0 | probabilities of half 1; PV of half 1.
+  auto tile_fast = [&](auto masked_tag, const lds_char* kl, const lds_char* vb, int k0) {
+    bf16x8 ka[8], pf[4], va[2][4];
+    read_k(kl, 0, ka);
+    const f32x16 s0 = qk(masked_tag, ka, 0, k0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_k(kl, 1, ka);
+    const f32x16 s1 = qk(masked_tag, ka, 1, k0);
+    probs(s0, 0.f, pf[0], pf[1]);
+    read_v2(vb, 0, va);
+    interleave(std::integral_constant<int, 8>{}, std::integral_constant<int, 3>{});
+    __builtin_amdgcn_sched_barrier(0);
+    pv2(va, pf, 0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pf[j], lacc, 0, 0, 0);
+    probs(s1, 0.f, pf[2], pf[3]);
+    interleave(std::integral_constant<int, 10>{}, std::integral_constant<int, 3>{});
+    __builtin_amdgcn_sched_barrier(0);
+    read_v2(vb, 2, va);
+    pv2(va, pf, 2);
+#pragma unroll
+    for (int j = 2; j < 4; ++j) lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pf[j], lacc, 0, 0, 0);
+  };
+  // ---- exact tile (the redo): streaming softmax with running maxima and
+  // fp32 row sums on the vector ALU.
+  auto tile_exact = [&](const lds_char* kl, const lds_char* vb, int k0) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      bf16x8 ka[8], pf[4];
+      read_k(kl, mb, ka);
+      const f32x16 sc = qk(std::true_type{}, ka, mb, k0);
+      const float mx = pair_max(max16(sc));
+      if (mx > mref) {
+        const float alpha = __builtin_amdgcn_exp2f(mref - mx);
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+        mref = mx;
+      }
+      const float m = (mref == -INFINITY) ? 0.f : mref;
+      lsum += probs_sum(sc, m, pf[2 * mb], pf[2 * mb + 1]);
+      bf16x8 va[2][4];
+      read_v2(vb, 2 * mb, va);
+      pv2(va, pf, 2 * mb);
+    }
+  };
+
+  // Walk the tiles from the last to the first; tiles [ktB, kt1] hold keys past
+  // some row's position, tiles [kt0, ktA) keys that may have left some row's
+  // window; only those take the mask, each run in a loop of its own.
+  const int ktB = max(kt0, min(kt1 + 1, (p0 + 1) / kBK));
+  const int xa = p0 + P - p.window;
+  const int ktA = (WINDOWED && xa > 0) ? min(ktB, max(kt0, (xa + kBK - 1) / kBK)) : kt0;
+  auto walk = [&](auto tile_fn, int kt_hi, int kt_lo) {
+    for (int kt = kt_hi; kt >= kt_lo; --kt) {
+      const int buf = (kt1 - kt) & 1;
+      wait_vmem<0>();   // this wave's loads of tile kt have landed
+      __syncthreads();  // every wave's have; the previous tile (or the query rows) fully read
+      if (kt > kt0) issue_tile(kt - 1, buf ^ 1);
+      tile_fn((const lds_char*)&lds_k[buf * kTileChunks], (const lds_char*)&lds_v[buf * kTileChunks], kt * kBK);
+    }
+  };
+  auto fast_masked = [&](const lds_char* kl, const lds_char* vb, int k0) { tile_fast(std::true_type{}, kl, vb, k0); };
+  auto fast_open = [&](const lds_char* kl, const lds_char* vb, int k0) { tile_fast(std::false_type{}, kl, vb, k0); };
+  auto reset = [&](float m0) {
+    mref = m0;
+    lsum = 0.f;
+    lacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
+  };
+
+  reset(0.f);
+  __builtin_amdgcn_s_setprio(0);
+  walk(fast_masked, kt1, ktB);
+  walk(fast_open, ktB - 1, ktA);
+  if constexpr (WINDOWED) walk(fast_masked, ktA - 1, kt0);
+  float lrow;
+  {
+    const float e0 = __shfl(lacc[0], l32 & 15);
+    const float e1 = __shfl(lacc[1], l32 & 15);
+    lrow = (l32 < 16) ? e0 : e1;
+  }
+  // The fast pass is kept unless a row's sum left [2^-64, 2^65) or a sum or an
+  // output is not finite; then the work-group redoes its rows exactly.
+  {
+    float osum = 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) osum += o[db][e];
+    const bool bad = !positive_in_binade_range(lrow, -kFastSumBinades, kFastSumBinades) || !finite_bits(osum);
+    const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+    if (lane == 0) redo_vote[w] = wave_bad ? 1 : 0;
+    __syncthreads();
+    if ((redo_vote[0] | redo_vote[1] | redo_vote[2] | redo_vote[3]) != 0) {
+      reset(sink_t());
+      issue_tile(kt1, 0);
+      walk(tile_exact, kt1, kt0);
+      lrow = pair_sum(lsum);
+    }
+  }
+
+  // ---- epilogue: the sink's term, 1 / l, bf16, store
+  float lt = lrow;
+  if (p.sinks) lt += __builtin_amdgcn_exp2f(sink_t() - mref);
+  const float inv = 1.f / lt;
+  if (pos < L) {
+    uint16_t* orow = p.out + ((int64_t)(s + pos) * Hq + head) * kD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int vg = 0; vg < 4; ++vg) {
+        const int d = 32 * db + 8 * vg + 4 * hi;
+        bf16x4 val;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = (__bf16)(o[db][4 * vg + e] * inv);
+        *(bf16x4*)(orow + d) = val;
+      }
+  }
+}
+
+template <int G>
+hipError_t launch_g(const Params& kp, int64_t grid, bool windowed, hipStream_t stream) {
+  const dim3 gd((unsigned)grid), bd(kThreads);
+  if (windowed)
+    hipLaunchKernelGGL((prefill_fwd_d128<G, true>), gd, bd, 0, stream, kp);
+  else
+    hipLaunchKernelGGL((prefill_fwd_d128<G, false>), gd, bd, 0, stream, kp);
+  return hipGetLastError();
+}
+
+int64_t pblocks128(const PrefillArgs& a) {
+  const int P = kRows / (a.n_q_heads / a.n_kv_heads);
+  return ((int64_t)a.max_seqlen + P - 1) / P;
+}
+
+}  // namespace
+
+int64_t prefill_grid_size_d128(const PrefillArgs& a) {
+  if (a.block_table) return -1;  // no paged form at this width
+  if (((int64_t)a.max_seqlen + kBK) * a.n_kv_heads * kRowBytes > 0x7fffffffLL) return -1;
+  if (((int64_t)a.max_seqlen + kRows) * a.n_q_heads * kRowBytes > 0x7fffffffLL) return -1;
+  const int64_t n = pblocks128(a) * (int64_t)a.n_seqs * (int64_t)a.n_kv_heads;
+  if (n > 0x7fffffffLL) return -1;
+  return n;
+}
+
+hipError_t launch_prefill_d128(const PrefillArgs& a, hipStream_t stream) {
+  const int64_t grid = prefill_grid_size_d128(a);
+  if (grid <= 0) return hipSuccess;
+  Params kp;
+  kp.q = static_cast<const uint16_t*>(a.q);
+  kp.k = static_cast<const uint16_t*>(a.k);
+  kp.v = static_cast<const uint16_t*>(a.v);
+  kp.sinks = a.sinks;
+  kp.cu = a.cu_seqlens;
+  kp.out = static_cast<uint16_t*>(a.out);
+  kp.n_kv_heads = a.n_kv_heads;
+  kp.n_seqs = a.n_seqs;
+  kp.n_pblocks = (int32_t)pblocks128(a);
+  kp.window = a.window > 0 ? a.window : 0;
+  kp.c = (float)((double)a.softmax_scale * 1.4426950408889634);
+  const bool windowed = a.window > 0;
+  (void)hipGetLastError();
+  switch (a.n_q_heads / a.n_kv_heads) {
+    case 1: return launch_g<1>(kp, grid, windowed, stream);
+    case 2: return launch_g<2>(kp, grid, windowed, stream);
+    case 4: return launch_g<4>(kp, grid, windowed, stream);
+    case 8: return launch_g<8>(kp, grid, windowed, stream);
+    case 16: return launch_g<16>(kp, grid, windowed, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace tsmha

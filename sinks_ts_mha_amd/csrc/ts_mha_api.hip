@@ -156,7 +156,7 @@ extern "C" int ts_mha_prefill(const void* q, const void* k, const void* v, const
   if (n_q_heads <= 0 || n_kv_heads <= 0 || n_seqs < 0 || max_seqlen < 0) return TS_MHA_ERR_BAD_SHAPE;
   if (n_q_heads % n_kv_heads != 0) return TS_MHA_ERR_BAD_SHAPE;
   const int32_t G = n_q_heads / n_kv_heads;
-  if (head_dim != 64) return TS_MHA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return TS_MHA_ERR_UNSUPPORTED;
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return TS_MHA_ERR_UNSUPPORTED;
   if (!isfinite(softmax_scale) || !(softmax_scale > 0.f)) return TS_MHA_ERR_BAD_SCALE;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
@@ -176,7 +176,7 @@ extern "C" int ts_mha_prefill(const void* q, const void* k, const void* v, const
   a.softmax_scale = softmax_scale;
   a.n_seqs = n_seqs;
   a.max_seqlen = max_seqlen;
-  const int64_t grid = tsmha::prefill_grid_size(a);
+  const int64_t grid = head_dim == 128 ? tsmha::prefill_grid_size_d128(a) : tsmha::prefill_grid_size(a);
   if (grid < 0) return TS_MHA_ERR_BAD_SHAPE;
 
   const int dev_rc = check_device();
@@ -190,7 +190,7 @@ extern "C" int ts_mha_prefill(const void* q, const void* k, const void* v, const
   }
   if (grid == 0) return TS_MHA_OK;
 
-  const hipError_t err = tsmha::launch_prefill(a, st);
+  const hipError_t err = head_dim == 128 ? tsmha::launch_prefill_d128(a, st) : tsmha::launch_prefill(a, st);
   if (err != hipSuccess) {
     snprintf(g_launch_msg, sizeof g_launch_msg, "%s", hipGetErrorString(err));
     return TS_MHA_ERR_LAUNCH;
@@ -324,8 +324,8 @@ extern "C" const char* ts_mha_strerror(int code) {
              "max_seqlen must be >= 0, the launch grid must fit; for the cache calls page_size a power "
              "of two >= 16, n_pages and pages_per_seq > 0, max_seqlen_k <= pages_per_seq * page_size";
     case TS_MHA_ERR_UNSUPPORTED:
-      return "unsupported configuration: head_dim must be 64 and n_q_heads / n_kv_heads one of "
-             "1, 2, 4, 8, 16";
+      return "unsupported configuration: head_dim must be 64 (or 128 for ts_mha_prefill) and "
+             "n_q_heads / n_kv_heads one of 1, 2, 4, 8, 16";
     case TS_MHA_ERR_BAD_SCALE: return "softmax_scale must be finite and > 0";
     case TS_MHA_ERR_ALIGN:
       return "misaligned pointer: q, k, v (or the caches), out need 16-byte alignment, sinks, "

@@ -86,6 +86,19 @@ WORKLOADS = {
         notes="1 sequence of 32768 tokens, 64 q / 8 KV heads, full causal, sinks"),
 }
 
+# The other head width of the kernel traits the TokenSpeed-kernel README lists
+# ("Public API"): head_dim 128 on the GPT-OSS layer shape (64 q / 8 KV heads,
+# 4 x 2048 packed, sinks), full causal and with a 128-key window; scale 1/sqrt(128).
+D128_WORKLOADS = {
+    "d128_full_4x2048": Workload(
+        "d128_full_4x2048", (2048,) * 4, 64, 8, head_dim=128, softmax_scale=128 ** -0.5,
+        notes="head_dim 128: 4 x 2048 packed, 64 q / 8 KV heads, full causal, sinks"),
+    "d128_window128_4x2048": Workload(
+        "d128_window128_4x2048", (2048,) * 4, 64, 8, head_dim=128, window=128,
+        softmax_scale=128 ** -0.5,
+        notes="head_dim 128: 4 x 2048 packed, 64 q / 8 KV heads, window 128, sinks"),
+}
+
 # The workload a benchmark step runs by default: the full-causal GPT-OSS layer.
 DEFAULT_BENCH_WORKLOAD = "gptoss_full_4x2048"
 
@@ -102,9 +115,12 @@ SWEEP = {
 
 
 def get(name: str):
-    """A named workload: one of WORKLOADS, a chart point of SWEEP, or a CACHE_WORKLOADS entry."""
+    """A named workload: one of WORKLOADS or D128_WORKLOADS, a chart point of SWEEP, or a
+    CACHE_WORKLOADS entry."""
     if name in WORKLOADS:
         return WORKLOADS[name]
+    if name in D128_WORKLOADS:
+        return D128_WORKLOADS[name]
     if name in SWEEP:
         return SWEEP[name]
     if name in CACHE_WORKLOADS:
