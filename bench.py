@@ -50,13 +50,14 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA peak
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E bandwidth
-KERNEL_SOURCE = os.path.join(ROOT, "sinks_ts_mha_amd", "csrc", "prefill_fwd.hip")
+KERNEL_SOURCES = {64: os.path.join(ROOT, "sinks_ts_mha_amd", "csrc", "prefill_fwd.hip"),
+                  128: os.path.join(ROOT, "sinks_ts_mha_amd", "csrc", "prefill_fwd_d128.hip")}
 METRIC = "prefill attention TFLOP/s (unmasked pairs) and % of MI355X bf16 MFMA peak"
 
 
-def source_sha() -> str:
-    """Hash of the kernel source's code: comments and whitespace do not count."""
-    text = open(KERNEL_SOURCE).read()
+def source_sha(head_dim: int = 64) -> str:
+    """Hash of the prefill kernel source's code for head_dim: comments and whitespace do not count."""
+    text = open(KERNEL_SOURCES[head_dim]).read()
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     text = " ".join(text.split())
@@ -73,7 +74,8 @@ def read_traffic(workload: str):
         m = re.match(r"^([A-Za-z0-9_]+):\s*(.+?)\s*$", line)
         if m:
             kv[m.group(1)] = m.group(2)
-    if kv.get("source_sha256") != source_sha():
+    from sinks_ts_mha_amd import workloads
+    if kv.get("source_sha256") != source_sha(workloads.get(workload).head_dim):
         return None
     try:
         fetch = float(kv["FETCH_SIZE_KiB_per_dispatch"]) * 1024 * float(kv["fetch_scale"])

@@ -301,29 +301,41 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
   };
 
   // ---- fast tile: probabilities against reference 1, row sums on the matrix
-  // pipe.  Four steps: scores of key half 0; scores of half 1 | probabilities
-  // of half 0; PV of half 0 | probabilities of half 1; PV of half 1.
+  // pipe.  Scores of key half 0; scores of half 1 | probabilities of half 0;
+  // then the four PV steps with their row sums, the probabilities of half 1
+  // interleaved, each step's V^T fragments read one step ahead (16 VGPRs at
+  // a time, which leaves the compiler room to keep the K reads ahead of the
+  // score MFMAs).
   auto tile_fast = [&](auto masked_tag, const lds_char* kl, const lds_char* vb, int k0) {
-    bf16x8 ka[8], pf[4], va[2][4];
+    bf16x8 ka[8], pf[4], va[4], vn[4];
     read_k(kl, 0, ka);
     const f32x16 s0 = qk(masked_tag, ka, 0, k0);
     __builtin_amdgcn_sched_barrier(0);
     read_k(kl, 1, ka);
     const f32x16 s1 = qk(masked_tag, ka, 1, k0);
     probs(s0, 0.f, pf[0], pf[1]);
-    read_v2(vb, 0, va);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) va[db] = read_v(vb, 0, db);
     interleave(std::integral_constant<int, 8>{}, std::integral_constant<int, 3>{});
     __builtin_amdgcn_sched_barrier(0);
-    pv2(va, pf, 0);
+    auto pv_step = [&](const bf16x8 (&v)[4], const bf16x8& pfrag) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pf[j], lacc, 0, 0, 0);
+      for (int db = 0; db < 4; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[db], pfrag, o[db], 0, 0, 0);
+      lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pfrag, lacc, 0, 0, 0);
+    };
+#pragma unroll
+    for (int db = 0; db < 4; ++db) vn[db] = read_v(vb, 1, db);
+    pv_step(va, pf[0]);
     probs(s1, 0.f, pf[2], pf[3]);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) va[db] = read_v(vb, 2, db);
+    pv_step(vn, pf[1]);
     interleave(std::integral_constant<int, 10>{}, std::integral_constant<int, 3>{});
     __builtin_amdgcn_sched_barrier(0);
-    read_v2(vb, 2, va);
-    pv2(va, pf, 2);
 #pragma unroll
-    for (int j = 2; j < 4; ++j) lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pf[j], lacc, 0, 0, 0);
+    for (int db = 0; db < 4; ++db) vn[db] = read_v(vb, 3, db);
+    pv_step(va, pf[2]);
+    pv_step(vn, pf[3]);
   };
   // ---- exact tile (the redo): streaming softmax with running maxima and
   // fp32 row sums on the vector ALU.
