@@ -573,24 +573,46 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
     }
   }
 
-  // ---- epilogue: add the sink's term to the row sum, normalise, store
+  // ---- epilogue: add the sink's term to the row sum, normalise, store.
+  // The rows go out through LDS: each wave writes its 64 normalised rows into
+  // its own part of the query staging area (unused since the prologue), in
+  // the staging layout, and reads them back one row per 8 lanes, so that each
+  // store instruction writes 8 whole 128-byte rows (1 KiB contiguous when the
+  // G heads of a position are) instead of 16-byte pieces of 32 rows.  Rows
+  // past the sequence end fall outside the output descriptor's range and are
+  // dropped.
+  // The lane index is laundered so that no address term of the query loads,
+  // which share these offsets, is kept live through the walk to be reused.
+  int el = lane;
+  asm volatile("" : "+v"(el));
+  const int el32 = el & 31, ehi = el >> 5;
+  u32x2* const lds_o = reinterpret_cast<u32x2*>(&lds_q[w * 64 * kChunks]);
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     float lt = lrow[nb];
     if (p.sinks) lt += __builtin_amdgcn_exp2f(sink_t(nb) - mref[nb]);
     const float inv = 1.f / lt;
-    if (pos[nb] < L) {
-      uint16_t* orow = p.out + ((int64_t)(s + pos[nb]) * Hq + head[nb]) * kD;
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < 2; ++db)
 #pragma unroll
-        for (int vg = 0; vg < 4; ++vg) {
-          const int d = 32 * db + 8 * vg + 4 * hi;
-          bf16x4 val;
+      for (int vg = 0; vg < 4; ++vg) {
+        // head_dim elements 32 db + 8 vg + 4 hi .. + 3: half hi of chunk 4 db + vg
+        bf16x4 val;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) val[e] = (__bf16)(o[db][nb][4 * vg + e] * inv);
-          *(bf16x4*)(orow + d) = val;
-        }
+        for (int e = 0; e < 4; ++e) val[e] = (__bf16)(o[db][nb][4 * vg + e] * inv);
+        lds_o[2 * swz(32 * nb + el32, 4 * db + vg) + ehi] = __builtin_bit_cast(u32x2, val);
+      }
+  }
+  {
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.out + (int64_t)s * Hq * kD), 0, L * Hq * kRowBytes, kBufferConfig);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int row = 8 * it + (el >> 3);  // within the wave's 64 rows
+      const int r = 64 * w + row;
+      const int ch = el & 7;
+      const u32x4 x = lds_q[w * 64 * kChunks + swz(row, ch)];
+      __builtin_amdgcn_raw_buffer_store_b128(x, ro, ((p0 + r / G) * Hq + g * G + r % G) * kRowBytes + ch * 16, 0, 0);
     }
   }
 }

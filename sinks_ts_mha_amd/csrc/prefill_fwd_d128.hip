@@ -421,22 +421,45 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
     }
   }
 
-  // ---- epilogue: the sink's term, 1 / l, bf16, store
+  // ---- epilogue: the sink's term, 1 / l, bf16, store.  The rows go out
+  // through LDS so that each store instruction writes 4 whole 256-byte rows
+  // instead of 16-byte pieces of 32 rows: each wave writes its 32 rows, in
+  // the staging layout, into its own 8 KiB of the slot that does not hold
+  // tile kt0 (every wave finished reading that slot before the barrier that
+  // opened tile kt0, or, with a single tile, before the first barrier), and
+  // reads them back 16 lanes per row.  Rows past the sequence end fall outside
+  // the output descriptor's range and are dropped.  The lane index is
+  // laundered so that no address term of the query loads, which share these
+  // offsets, is kept live through the walk.
+  int el = lane;
+  asm volatile("" : "+v"(el));
+  const int el32 = el & 31, ehi = el >> 5;
+  const int free_slot = ((kt1 - kt0) & 1) ^ 1;
+  lds_char* const ob = (w < 2 ? (lds_char*)lds_k : (lds_char*)lds_v) + free_slot * kTileBytes + (w & 1) * kQW * kRowBytes;
   float lt = lrow;
   if (p.sinks) lt += __builtin_amdgcn_exp2f(sink_t() - mref);
   const float inv = 1.f / lt;
-  if (pos < L) {
-    uint16_t* orow = p.out + ((int64_t)(s + pos) * Hq + head) * kD;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int vg = 0; vg < 4; ++vg) {
-        const int d = 32 * db + 8 * vg + 4 * hi;
-        bf16x4 val;
+    for (int vg = 0; vg < 4; ++vg) {
+      // head_dim elements 32 db + 8 vg + 4 hi .. + 3: half hi of chunk 4 db + vg
+      bf16x4 val;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) val[e] = (__bf16)(o[db][4 * vg + e] * inv);
-        *(bf16x4*)(orow + d) = val;
-      }
+      for (int e = 0; e < 4; ++e) val[e] = (__bf16)(o[db][4 * vg + e] * inv);
+      *(u32x2*)(ob + pos16(el32, 4 * db + vg) * 16 + 8 * ehi) = __builtin_bit_cast(u32x2, val);
+    }
+  {
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.out + (int64_t)s * Hq * kD), 0, L * Hq * kRowBytes, kBufferConfig);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 4 * i + (el >> 4);  // within the wave's 32 rows
+      const int r = kQW * w + row;
+      const int ch = el & 15;
+      const u32x4 x = *(const u32x4*)(ob + pos16(row, ch) * 16);
+      __builtin_amdgcn_raw_buffer_store_b128(x, ro, ((p0 + r / G) * Hq + g * G + r % G) * kRowBytes + ch * 16, 0, 0);
+    }
   }
 }
 
