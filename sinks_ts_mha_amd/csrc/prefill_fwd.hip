@@ -464,6 +464,28 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
     row_sums(pf, 1, 1);
   };
 
+  // ---- half tile: only key half mb of the tile, masked, for a tile whose
+  // other 32 keys are hidden from every row (the upper half of a diagonal
+  // tile whose rows all sit in its lower half, or the lower half of a tile
+  // that has left every row's window).
+  auto tile_half = [&](auto mb_tag, const u32x4* kl, lds_char* vb, int k0) {
+    constexpr int mb = decltype(mb_tag)::value;
+    bf16x8 ka[4], pf[4][2], va[2][2];
+    read_k(kl, mb, ka);
+    const f32x16 s0 = qk(std::true_type{}, ka, mb, 0, k0);
+    const f32x16 s1 = qk(std::true_type{}, ka, mb, 1, k0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_v(vb, 2 * mb, va[0]);
+    read_v(vb, 2 * mb + 1, va[1]);
+    block_probs_fast(s0, pf[2 * mb][0], pf[2 * mb + 1][0]);
+    block_probs_fast(s1, pf[2 * mb][1], pf[2 * mb + 1][1]);
+    __builtin_amdgcn_sched_barrier(0);
+    pv(va, pf, mb, 0);
+    row_sums(pf, mb, 0);
+    pv(va, pf, mb, 1);
+    row_sums(pf, mb, 1);
+  };
+
   // ---- exact tile: streaming softmax with running maxima and fp32 row sums
   // on the vector ALU.  It runs every tile of a work-group whose fast pass
   // left range.  Each key half raises the row maxima, rescales the
@@ -518,6 +540,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   auto exact_masked = [&](const u32x4* kl, lds_char* vb, int k0) { tile_exact(std::true_type{}, kl, vb, k0); };
   auto fast_masked = [&](const u32x4* kl, lds_char* vb, int k0) { tile_fast(std::true_type{}, kl, vb, k0); };
   auto fast_open = [&](const u32x4* kl, lds_char* vb, int k0) { tile_fast(std::false_type{}, kl, vb, k0); };
+  auto half_lo = [&](const u32x4* kl, lds_char* vb, int k0) { tile_half(std::integral_constant<int, 0>{}, kl, vb, k0); };
+  auto half_hi = [&](const u32x4* kl, lds_char* vb, int k0) { tile_half(std::integral_constant<int, 1>{}, kl, vb, k0); };
   auto reset = [&]() {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
@@ -534,9 +558,21 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   reset();
   mref[0] = mref[1] = 0.f;  // the fast pass measures every probability against 1
   __builtin_amdgcn_s_setprio(0);
-  walk(fast_masked, kt1, ktB);
+  // Tile kt1 (always a masked one) skips its upper 32 keys when they lie past
+  // every row's position; with a window, tile kt0 (then always masked too)
+  // skips its lower 32 keys when they lie before every row's window.  The two
+  // never fall on one tile (first <= last).
+  const bool hi_half_hidden = (last & (kBK - 1)) < kBK / 2;
+  const bool lo_half_hidden = WINDOWED && (first & (kBK - 1)) >= kBK / 2;
+  const int top = hi_half_hidden ? kt1 - 1 : kt1;
+  const int bot = lo_half_hidden ? kt0 + 1 : kt0;
+  if (hi_half_hidden) walk(half_lo, kt1, kt1);
+  walk(fast_masked, top, max(ktB, bot));
   walk(fast_open, ktB - 1, ktA);
-  if constexpr (WINDOWED) walk(fast_masked, ktA - 1, kt0);
+  if constexpr (WINDOWED) {
+    walk(fast_masked, ktA - 1, bot);
+    if (lo_half_hidden) walk(half_hi, kt0, kt0);
+  }
   // A row's sum from the row-sum accumulators: query q of block nb sits in
   // lane q % 16, element q / 16.
   float lrow[2];

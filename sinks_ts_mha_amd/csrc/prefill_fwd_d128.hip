@@ -337,6 +337,22 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
     pv_step(va, pf[2]);
     pv_step(vn, pf[3]);
   };
+  // ---- half tile: only key half mb, masked, for a tile whose other 32 keys
+  // are hidden from every row (past every row's position, or before every
+  // row's window).
+  auto tile_half = [&](auto mb_tag, const lds_char* kl, const lds_char* vb, int k0) {
+    constexpr int mb = decltype(mb_tag)::value;
+    bf16x8 ka[8], pf[4], va[2][4];
+    read_k(kl, mb, ka);
+    const f32x16 sc = qk(std::true_type{}, ka, mb, k0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_v2(vb, 2 * mb, va);
+    probs(sc, 0.f, pf[2 * mb], pf[2 * mb + 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    pv2(va, pf, 2 * mb);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pf[2 * mb + j], lacc, 0, 0, 0);
+  };
   // ---- exact tile (the redo): streaming softmax with running maxima and
   // fp32 row sums on the vector ALU.
   auto tile_exact = [&](const lds_char* kl, const lds_char* vb, int k0) {
@@ -380,6 +396,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
   };
   auto fast_masked = [&](const lds_char* kl, const lds_char* vb, int k0) { tile_fast(std::true_type{}, kl, vb, k0); };
   auto fast_open = [&](const lds_char* kl, const lds_char* vb, int k0) { tile_fast(std::false_type{}, kl, vb, k0); };
+  auto half_lo = [&](const lds_char* kl, const lds_char* vb, int k0) { tile_half(std::integral_constant<int, 0>{}, kl, vb, k0); };
+  auto half_hi = [&](const lds_char* kl, const lds_char* vb, int k0) { tile_half(std::integral_constant<int, 1>{}, kl, vb, k0); };
   auto reset = [&](float m0) {
     mref = m0;
     lsum = 0.f;
@@ -392,9 +410,21 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
 
   reset(0.f);
   __builtin_amdgcn_s_setprio(0);
-  walk(fast_masked, kt1, ktB);
+  // Tile kt1 (always masked) skips its upper 32 keys when they lie past every
+  // row's position; with a window, tile kt0 (then always masked) skips its
+  // lower 32 keys when they lie before every row's window (never both on one
+  // tile: first <= last).
+  const bool hi_half_hidden = (last & (kBK - 1)) < kBK / 2;
+  const bool lo_half_hidden = WINDOWED && (first & (kBK - 1)) >= kBK / 2;
+  const int top = hi_half_hidden ? kt1 - 1 : kt1;
+  const int bot = lo_half_hidden ? kt0 + 1 : kt0;
+  if (hi_half_hidden) walk(half_lo, kt1, kt1);
+  walk(fast_masked, top, max(ktB, bot));
   walk(fast_open, ktB - 1, ktA);
-  if constexpr (WINDOWED) walk(fast_masked, ktA - 1, kt0);
+  if constexpr (WINDOWED) {
+    walk(fast_masked, ktA - 1, bot);
+    if (lo_half_hidden) walk(half_hi, kt0, kt0);
+  }
   float lrow;
   {
     const float e0 = __shfl(lacc[0], l32 & 15);
