@@ -57,7 +57,14 @@
 // matrix pipe and the vector ALU busy at the same time.  Tiles that need the
 // causal or window mask start their score accumulators from a 0 / -inf mask,
 // and run in loops of their own, so that each loop body holds a single kind of
-// tile.
+// tile.  A tile whose upper (or lower) 32 keys are hidden from every row of
+// the work-group computes only its other half (tile_half): its skipped keys
+// would add exact zeros.
+//
+// Output.  Each wave writes its normalised bf16 rows into its part of the
+// query staging area and reads them back whole, so every store instruction
+// writes complete 128-byte rows (1 KiB contiguous when the G heads of a
+// position are) rather than 16-byte pieces of 32 rows.
 #include "prefill_fwd.h"
 
 #include <math.h>
