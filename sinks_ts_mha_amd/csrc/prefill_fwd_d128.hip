@@ -234,12 +234,16 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
     f32x16 acc = {};
     if constexpr (MASKED) {
       const int di = pos - k0 - 4 * hi;
-      const int dw = di - p.window;
+      // hidden <=> cc > di, or (with a window) cc <= di - window: the sign
+      // bit of di - cc, or of cc - 1 - (di - window), selects the bits of
+      // -inf, else 0.  Unsigned arithmetic: the second difference can pass
+      // 2^31 only when cc > di, where the first is already negative.
+      const uint32_t udw = (uint32_t)di - (uint32_t)p.window;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int cc = 32 * mb + 8 * (e / 4) + (e % 4);
-        const bool vis = (cc <= di) && (!WINDOWED || cc > dw);
-        acc[e] = vis ? 0.f : -INFINITY;
+        const uint32_t t = WINDOWED ? (((uint32_t)di - cc) | ((uint32_t)cc - 1u - udw)) : ((uint32_t)di - cc);
+        acc[e] = __uint_as_float((uint32_t)((int32_t)t >> 31) & 0xff800000u);
       }
     }
 #pragma unroll

@@ -129,8 +129,9 @@ def test_bitwise_invariants_d128():
         alone = run_gpu(one).cpu()
         assert torch.equal(alone.view(torch.int16), packed[s:e].view(torch.int16)), f"sequence {b}"
     full = run_gpu(inp, window=0).cpu()
-    wide = run_gpu(inp, window=300).cpu()
-    assert torch.equal(full.view(torch.int16), wide.view(torch.int16)), "W >= L vs full"
+    for w in (300, 2**31 - 1):
+        wide = run_gpu(inp, window=w).cpu()
+        assert torch.equal(full.view(torch.int16), wide.view(torch.int16)), f"W={w} >= L vs full"
 
 
 def test_output_fully_overwritten_d128():

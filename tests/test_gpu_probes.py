@@ -189,7 +189,8 @@ def test_window_covering_equals_full_bitwise():
     inp = workloads.make_inputs(wl)
     say("window >= length vs full")
     full = run_gpu(inp).cpu()
-    for w in (1000, 5000):
+    # 2^31 - 1 also takes the mask's window arithmetic through its wrap-around
+    for w in (1000, 5000, 2**31 - 1):
         got = run_gpu(inp, window=w).cpu()
         assert torch.equal(got.view(torch.int16), full.view(torch.int16)), f"W={w}"
 
