@@ -91,6 +91,8 @@ constexpr int kTileChunks = kBK * kChunks;    // 16-byte chunks per tile
 constexpr int kTileBytes = kTileChunks * 16;
 constexpr int kFastSumBinades = 64;  // the fast pass keeps row sums in [2^-64, 2^65)
 constexpr int kSlots = 2;                     // LDS buffers for K and for V tiles
+constexpr int kMaskCausal = 1;                // mask kinds: key past the row's position
+constexpr int kMaskWindow = 2;                // ... key before the row's window
 
 
 struct KParams {
@@ -350,10 +352,12 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   // visible key, -inf for a hidden one), so the MFMA applies it.  Element e
   // holds key k0 + 4 hi + 32 mb + 8 (e / 4) + e % 4, compared against the
   // lane's diagonal offset so that the key offset stays an immediate.
-  auto qk = [&](auto masked_tag, const bf16x8 (&ka)[4], int mb, int nb, int k0) -> f32x16 {
-    constexpr bool MASKED = decltype(masked_tag)::value;
+  // Mask kinds: 0 none, 1 causal only, 2 window only, 3 both (kMaskCausal | kMaskWindow).
+  auto qk = [&](auto mask_tag, const bf16x8 (&ka)[4], int mb, int nb, int k0) -> f32x16 {
+    constexpr int M = decltype(mask_tag)::value;
+    static_assert(WINDOWED || (M & kMaskWindow) == 0, "window mask without a window");
     f32x16 acc = {};
-    if constexpr (MASKED) {
+    if constexpr (M != 0) {
       const int di = qoff + pos[nb] - k0 - 4 * hi;
       // hidden <=> cc > di, or (with a window) cc <= di - window: the sign
       // bit of di - cc, or of cc - 1 - (di - window), selects the bits of
@@ -363,7 +367,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int cc = 32 * mb + 8 * (e / 4) + (e % 4);
-        const uint32_t t = WINDOWED ? (((uint32_t)di - cc) | ((uint32_t)cc - 1u - udw)) : ((uint32_t)di - cc);
+        uint32_t t = 0;
+        if constexpr (M & kMaskCausal) t |= (uint32_t)di - cc;
+        if constexpr (M & kMaskWindow) t |= (uint32_t)cc - 1u - udw;
         acc[e] = __uint_as_float((uint32_t)((int32_t)t >> 31) & 0xff800000u);
       }
     }
@@ -438,22 +444,22 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   //   4: PV (0,1)     | probs (1,1)    5: PV (1,0) (1,1)
   using I4 = std::integral_constant<int, 4>;
   using I6 = std::integral_constant<int, 6>;
-  auto tile_fast = [&](auto masked_tag, const u32x4* kl, lds_char* vb, int k0) {
+  auto tile_fast = [&](auto mask_tag, const u32x4* kl, lds_char* vb, int k0) {
     constexpr int nv = 6;  // vector instructions after each score MFMA
     constexpr int nw = 4;  // ... after each PV or row-sum MFMA
     bf16x8 ka[4], kb[4], pf[4][2], va[2][2], vc[2][2];
     read_k(kl, 0, ka);
     read_k(kl, 1, kb);
-    const f32x16 s00 = qk(masked_tag, ka, 0, 0, k0);
-    const f32x16 s01 = qk(masked_tag, ka, 0, 1, k0);
+    const f32x16 s00 = qk(mask_tag, ka, 0, 0, k0);
+    const f32x16 s01 = qk(mask_tag, ka, 0, 1, k0);
     __builtin_amdgcn_sched_barrier(0);
     read_v(vb, 0, va[0]);
     read_v(vb, 1, va[1]);
-    const f32x16 s10 = qk(masked_tag, kb, 1, 0, k0);
+    const f32x16 s10 = qk(mask_tag, kb, 1, 0, k0);
     block_probs_fast(s00, pf[0][0], pf[1][0]);
     interleave(I4{}, std::integral_constant<int, nv>{});
     __builtin_amdgcn_sched_barrier(0);
-    const f32x16 s11 = qk(masked_tag, kb, 1, 1, k0);
+    const f32x16 s11 = qk(mask_tag, kb, 1, 1, k0);
     block_probs_fast(s01, pf[0][1], pf[1][1]);
     interleave(I4{}, std::integral_constant<int, nv>{});
     __builtin_amdgcn_sched_barrier(0);
@@ -479,12 +485,12 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   // other 32 keys are hidden from every row (the upper half of a diagonal
   // tile whose rows all sit in its lower half, or the lower half of a tile
   // that has left every row's window).
-  auto tile_half = [&](auto mb_tag, const u32x4* kl, lds_char* vb, int k0) {
+  auto tile_half = [&](auto mb_tag, auto mask_tag, const u32x4* kl, lds_char* vb, int k0) {
     constexpr int mb = decltype(mb_tag)::value;
     bf16x8 ka[4], pf[4][2], va[2][2];
     read_k(kl, mb, ka);
-    const f32x16 s0 = qk(std::true_type{}, ka, mb, 0, k0);
-    const f32x16 s1 = qk(std::true_type{}, ka, mb, 1, k0);
+    const f32x16 s0 = qk(mask_tag, ka, mb, 0, k0);
+    const f32x16 s1 = qk(mask_tag, ka, mb, 1, k0);
     __builtin_amdgcn_sched_barrier(0);
     read_v(vb, 2 * mb, va[0]);
     read_v(vb, 2 * mb + 1, va[1]);
@@ -501,14 +507,14 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   // on the vector ALU.  It runs every tile of a work-group whose fast pass
   // left range.  Each key half raises the row maxima, rescales the
   // accumulators, then adds its probabilities.
-  auto tile_exact = [&](auto masked_tag, const u32x4* kl, lds_char* vb, int k0) {
+  auto tile_exact = [&](auto mask_tag, const u32x4* kl, lds_char* vb, int k0) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       bf16x8 ka[4], pf[4][2], va[2][2];
       read_k(kl, mb, ka);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        const f32x16 sc = qk(masked_tag, ka, mb, nb, k0);
+        const f32x16 sc = qk(mask_tag, ka, mb, nb, k0);
         const float mx = pair_max(max16(sc));
         if (mx > mref[nb]) {
           const float alpha = __builtin_amdgcn_exp2f(mref[nb] - mx);
@@ -548,11 +554,21 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
       tile_fn(&lds_k[buf * kTileChunks], (lds_char*)&lds_v[buf * kTileChunks], kt * kBK);
     }
   };
-  auto exact_masked = [&](const u32x4* kl, lds_char* vb, int k0) { tile_exact(std::true_type{}, kl, vb, k0); };
-  auto fast_masked = [&](const u32x4* kl, lds_char* vb, int k0) { tile_fast(std::true_type{}, kl, vb, k0); };
-  auto fast_open = [&](const u32x4* kl, lds_char* vb, int k0) { tile_fast(std::false_type{}, kl, vb, k0); };
-  auto half_lo = [&](const u32x4* kl, lds_char* vb, int k0) { tile_half(std::integral_constant<int, 0>{}, kl, vb, k0); };
-  auto half_hi = [&](const u32x4* kl, lds_char* vb, int k0) { tile_half(std::integral_constant<int, 1>{}, kl, vb, k0); };
+  using MNone = std::integral_constant<int, 0>;
+  using MCausal = std::integral_constant<int, kMaskCausal>;
+  using MWindow = std::integral_constant<int, WINDOWED ? kMaskWindow : 0>;
+  using MBoth = std::integral_constant<int, kMaskCausal | (WINDOWED ? kMaskWindow : 0)>;
+  using Lo = std::integral_constant<int, 0>;
+  using Hi = std::integral_constant<int, 1>;
+  auto exact_masked = [&](const u32x4* kl, lds_char* vb, int k0) { tile_exact(MBoth{}, kl, vb, k0); };
+  auto fast_both = [&](const u32x4* kl, lds_char* vb, int k0) { tile_fast(MBoth{}, kl, vb, k0); };
+  auto fast_causal = [&](const u32x4* kl, lds_char* vb, int k0) { tile_fast(MCausal{}, kl, vb, k0); };
+  auto fast_window = [&](const u32x4* kl, lds_char* vb, int k0) { tile_fast(MWindow{}, kl, vb, k0); };
+  auto fast_open = [&](const u32x4* kl, lds_char* vb, int k0) { tile_fast(MNone{}, kl, vb, k0); };
+  auto half_lo_both = [&](const u32x4* kl, lds_char* vb, int k0) { tile_half(Lo{}, MBoth{}, kl, vb, k0); };
+  auto half_lo_causal = [&](const u32x4* kl, lds_char* vb, int k0) { tile_half(Lo{}, MCausal{}, kl, vb, k0); };
+  auto half_hi_both = [&](const u32x4* kl, lds_char* vb, int k0) { tile_half(Hi{}, MBoth{}, kl, vb, k0); };
+  auto half_hi_window = [&](const u32x4* kl, lds_char* vb, int k0) { tile_half(Hi{}, MWindow{}, kl, vb, k0); };
   auto reset = [&]() {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
@@ -577,12 +593,25 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   const bool lo_half_hidden = WINDOWED && (first & (kBK - 1)) >= kBK / 2;
   const int top = hi_half_hidden ? kt1 - 1 : kt1;
   const int bot = lo_half_hidden ? kt0 + 1 : kt0;
-  if (hi_half_hidden) walk(half_lo, kt1, kt1);
-  walk(fast_masked, top, max(ktB, bot));
+  // Which tests a masked tile needs.  Tiles [ktB, kt1] need the causal one,
+  // and the window one only if the window reaches them: it can hide a key of
+  // tile kt from some row only if kt * kBK <= last - window.  Tiles below ktA
+  // (below ktB) hold no key past any row's position: the window test alone.
+  const bool diag_windowed = WINDOWED && last - p.window >= 0 && ktB <= (last - p.window) / kBK;
+  if (!WINDOWED || !diag_windowed) {
+    if (hi_half_hidden) walk(half_lo_causal, kt1, kt1);
+    walk(fast_causal, top, max(ktB, bot));
+  } else {
+    if (hi_half_hidden) walk(half_lo_both, kt1, kt1);
+    walk(fast_both, top, max(ktB, bot));
+  }
   walk(fast_open, ktB - 1, ktA);
   if constexpr (WINDOWED) {
-    walk(fast_masked, ktA - 1, bot);
-    if (lo_half_hidden) walk(half_hi, kt0, kt0);
+    walk(fast_window, ktA - 1, bot);
+    if (lo_half_hidden) {
+      if (kt0 < ktB) walk(half_hi_window, kt0, kt0);
+      else walk(half_hi_both, kt0, kt0);
+    }
   }
   // A row's sum from the row-sum accumulators: query q of block nb sits in
   // lane q % 16, element q / 16.

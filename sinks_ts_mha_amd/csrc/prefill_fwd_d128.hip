@@ -59,6 +59,8 @@ constexpr int kChunks = kRowBytes / 16;        // 16-byte chunks per row
 constexpr int kTileBytes = kBK * kRowBytes;    // 16 KiB
 constexpr int kTileChunks = kTileBytes / 16;
 constexpr int kFastSumBinades = 64;  // the fast pass keeps row sums in [2^-64, 2^65)
+constexpr int kMaskCausal = 1;       // mask kinds: key past the row's position
+constexpr int kMaskWindow = 2;       // ... key before the row's window
 
 struct Params {
   const uint16_t* q;
@@ -229,10 +231,12 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
   };
   // Scores of key half mb: element e holds key k0 + 32 mb + 8 (e / 4) + 4 hi + e % 4.
   // Masked tiles start the accumulator from the mask (0 visible, -inf hidden).
-  auto qk = [&](auto masked_tag, const bf16x8 (&ka)[8], int mb, int k0) -> f32x16 {
-    constexpr bool MASKED = decltype(masked_tag)::value;
+  // Mask kinds: 0 none, 1 causal only, 2 window only, 3 both.
+  auto qk = [&](auto mask_tag, const bf16x8 (&ka)[8], int mb, int k0) -> f32x16 {
+    constexpr int M = decltype(mask_tag)::value;
+    static_assert(WINDOWED || (M & kMaskWindow) == 0, "window mask without a window");
     f32x16 acc = {};
-    if constexpr (MASKED) {
+    if constexpr (M != 0) {
       const int di = pos - k0 - 4 * hi;
       // hidden <=> cc > di, or (with a window) cc <= di - window: the sign
       // bit of di - cc, or of cc - 1 - (di - window), selects the bits of
@@ -242,7 +246,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int cc = 32 * mb + 8 * (e / 4) + (e % 4);
-        const uint32_t t = WINDOWED ? (((uint32_t)di - cc) | ((uint32_t)cc - 1u - udw)) : ((uint32_t)di - cc);
+        uint32_t t = 0;
+        if constexpr (M & kMaskCausal) t |= (uint32_t)di - cc;
+        if constexpr (M & kMaskWindow) t |= (uint32_t)cc - 1u - udw;
         acc[e] = __uint_as_float((uint32_t)((int32_t)t >> 31) & 0xff800000u);
       }
     }
@@ -310,13 +316,13 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
   // interleaved, each step's V^T fragments read one step ahead (16 VGPRs at
   // a time, which leaves the compiler room to keep the K reads ahead of the
   // score MFMAs).
-  auto tile_fast = [&](auto masked_tag, const lds_char* kl, const lds_char* vb, int k0) {
+  auto tile_fast = [&](auto mask_tag, const lds_char* kl, const lds_char* vb, int k0) {
     bf16x8 ka[8], pf[4], va[4], vn[4];
     read_k(kl, 0, ka);
-    const f32x16 s0 = qk(masked_tag, ka, 0, k0);
+    const f32x16 s0 = qk(mask_tag, ka, 0, k0);
     __builtin_amdgcn_sched_barrier(0);
     read_k(kl, 1, ka);
-    const f32x16 s1 = qk(masked_tag, ka, 1, k0);
+    const f32x16 s1 = qk(mask_tag, ka, 1, k0);
     probs(s0, 0.f, pf[0], pf[1]);
 #pragma unroll
     for (int db = 0; db < 4; ++db) va[db] = read_v(vb, 0, db);
@@ -344,11 +350,11 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
   // ---- half tile: only key half mb, masked, for a tile whose other 32 keys
   // are hidden from every row (past every row's position, or before every
   // row's window).
-  auto tile_half = [&](auto mb_tag, const lds_char* kl, const lds_char* vb, int k0) {
+  auto tile_half = [&](auto mb_tag, auto mask_tag, const lds_char* kl, const lds_char* vb, int k0) {
     constexpr int mb = decltype(mb_tag)::value;
     bf16x8 ka[8], pf[4], va[2][4];
     read_k(kl, mb, ka);
-    const f32x16 sc = qk(std::true_type{}, ka, mb, k0);
+    const f32x16 sc = qk(mask_tag, ka, mb, k0);
     __builtin_amdgcn_sched_barrier(0);
     read_v2(vb, 2 * mb, va);
     probs(sc, 0.f, pf[2 * mb], pf[2 * mb + 1]);
@@ -364,7 +370,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
     for (int mb = 0; mb < 2; ++mb) {
       bf16x8 ka[8], pf[4];
       read_k(kl, mb, ka);
-      const f32x16 sc = qk(std::true_type{}, ka, mb, k0);
+      const f32x16 sc = qk(std::integral_constant<int, kMaskCausal | (WINDOWED ? kMaskWindow : 0)>{}, ka, mb, k0);
       const float mx = pair_max(max16(sc));
       if (mx > mref) {
         const float alpha = __builtin_amdgcn_exp2f(mref - mx);
@@ -398,10 +404,20 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
       tile_fn((const lds_char*)&lds_k[buf * kTileChunks], (const lds_char*)&lds_v[buf * kTileChunks], kt * kBK);
     }
   };
-  auto fast_masked = [&](const lds_char* kl, const lds_char* vb, int k0) { tile_fast(std::true_type{}, kl, vb, k0); };
-  auto fast_open = [&](const lds_char* kl, const lds_char* vb, int k0) { tile_fast(std::false_type{}, kl, vb, k0); };
-  auto half_lo = [&](const lds_char* kl, const lds_char* vb, int k0) { tile_half(std::integral_constant<int, 0>{}, kl, vb, k0); };
-  auto half_hi = [&](const lds_char* kl, const lds_char* vb, int k0) { tile_half(std::integral_constant<int, 1>{}, kl, vb, k0); };
+  using MNone = std::integral_constant<int, 0>;
+  using MCausal = std::integral_constant<int, kMaskCausal>;
+  using MWindow = std::integral_constant<int, WINDOWED ? kMaskWindow : 0>;
+  using MBoth = std::integral_constant<int, kMaskCausal | (WINDOWED ? kMaskWindow : 0)>;
+  using Lo = std::integral_constant<int, 0>;
+  using Hi = std::integral_constant<int, 1>;
+  auto fast_both = [&](const lds_char* kl, const lds_char* vb, int k0) { tile_fast(MBoth{}, kl, vb, k0); };
+  auto fast_causal = [&](const lds_char* kl, const lds_char* vb, int k0) { tile_fast(MCausal{}, kl, vb, k0); };
+  auto fast_window = [&](const lds_char* kl, const lds_char* vb, int k0) { tile_fast(MWindow{}, kl, vb, k0); };
+  auto fast_open = [&](const lds_char* kl, const lds_char* vb, int k0) { tile_fast(MNone{}, kl, vb, k0); };
+  auto half_lo_both = [&](const lds_char* kl, const lds_char* vb, int k0) { tile_half(Lo{}, MBoth{}, kl, vb, k0); };
+  auto half_lo_causal = [&](const lds_char* kl, const lds_char* vb, int k0) { tile_half(Lo{}, MCausal{}, kl, vb, k0); };
+  auto half_hi_both = [&](const lds_char* kl, const lds_char* vb, int k0) { tile_half(Hi{}, MBoth{}, kl, vb, k0); };
+  auto half_hi_window = [&](const lds_char* kl, const lds_char* vb, int k0) { tile_half(Hi{}, MWindow{}, kl, vb, k0); };
   auto reset = [&](float m0) {
     mref = m0;
     lsum = 0.f;
@@ -422,12 +438,24 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
   const bool lo_half_hidden = WINDOWED && (first & (kBK - 1)) >= kBK / 2;
   const int top = hi_half_hidden ? kt1 - 1 : kt1;
   const int bot = lo_half_hidden ? kt0 + 1 : kt0;
-  if (hi_half_hidden) walk(half_lo, kt1, kt1);
-  walk(fast_masked, top, max(ktB, bot));
+  // Tiles [ktB, kt1] need the causal test, and the window test only if the
+  // window reaches them (kt * kBK <= last - window); tiles below ktA hold no
+  // key past any row's position and need the window test alone.
+  const bool diag_windowed = WINDOWED && last - p.window >= 0 && ktB <= (last - p.window) / kBK;
+  if (!WINDOWED || !diag_windowed) {
+    if (hi_half_hidden) walk(half_lo_causal, kt1, kt1);
+    walk(fast_causal, top, max(ktB, bot));
+  } else {
+    if (hi_half_hidden) walk(half_lo_both, kt1, kt1);
+    walk(fast_both, top, max(ktB, bot));
+  }
   walk(fast_open, ktB - 1, ktA);
   if constexpr (WINDOWED) {
-    walk(fast_masked, ktA - 1, bot);
-    if (lo_half_hidden) walk(half_hi, kt0, kt0);
+    walk(fast_window, ktA - 1, bot);
+    if (lo_half_hidden) {
+      if (kt0 < ktB) walk(half_hi_window, kt0, kt0);
+      else walk(half_hi_both, kt0, kt0);
+    }
   }
   float lrow;
   {
