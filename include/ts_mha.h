@@ -53,9 +53,11 @@ extern "C" {
 #define TS_MHA_ERR_NULL_ARG (-1)     /* a required pointer is NULL */
 #define TS_MHA_ERR_BAD_SHAPE (-2)    /* heads <= 0, n_q_heads % n_kv_heads != 0, n_seqs < 0,
                                         max_seqlen < 0, the launch grid would overflow, or one
-                                        sequence's q rows ((max_seqlen + 256) * n_q_heads * 2 *
-                                        head_dim bytes) or k/v rows ((max_seqlen + 64) *
-                                        n_kv_heads * 2 * head_dim bytes) would exceed 2^31 - 1 */
+                                        sequence's q rows ((max_seqlen + R) * n_q_heads * 2 *
+                                        head_dim bytes, R = 256 at head_dim 64 and 128 at
+                                        head_dim 128: the rows of one work-group) or k/v rows
+                                        ((max_seqlen + 64) * n_kv_heads * 2 * head_dim bytes)
+                                        would exceed 2^31 - 1 */
 #define TS_MHA_ERR_UNSUPPORTED (-3)  /* head_dim not 64 (ts_mha_prefill: 64 or 128), or
                                         n_q_heads / n_kv_heads not in {1,2,4,8,16} */
 #define TS_MHA_ERR_BAD_SCALE (-4)    /* softmax_scale not finite or <= 0 */
