@@ -51,7 +51,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA peak
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E bandwidth
 KERNEL_SOURCES = {64: os.path.join(ROOT, "sinks_ts_mha_amd", "csrc", "prefill_fwd.hip"),
-                  128: os.path.join(ROOT, "sinks_ts_mha_amd", "csrc", "prefill_fwd_d128.hip")}
+                  128: os.path.join(ROOT, "sinks_ts_mha_amd", "csrc", "prefill_fwd_narrow.hip")}
 METRIC = "prefill attention TFLOP/s (unmasked pairs) and % of MI355X bf16 MFMA peak"
 
 

@@ -95,6 +95,12 @@ extern "C" {
  *               positions beyond it are not computed)
  *  stream       hipStream_t to enqueue on; NULL = the default stream
  *
+ *  At head_dim 64 the call picks between two kernels with identical results:
+ *  work-groups of 256 query rows, or of 128 when the former would give no
+ *  compute unit more than two work-groups (short or few sequences).  The
+ *  environment variable TS_MHA_PREFILL_KERNEL=wide|narrow forces one of them
+ *  (for tests and measurement); head_dim 128 always uses 128-row work-groups.
+ *
  *  Returns TS_MHA_OK or a TS_MHA_ERR_* code (see above).
  */
 int ts_mha_prefill(const void* q, const void* k, const void* v, const float* sinks,

@@ -21,7 +21,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libts_mha.so")
-SOURCES = ["prefill_fwd.hip", "prefill_fwd_d128.hip", "decode_fwd.hip", "ts_mha_api.hip"]
+SOURCES = ["prefill_fwd.hip", "prefill_fwd_narrow.hip", "decode_fwd.hip", "ts_mha_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-fno-honor-nans",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -36,9 +36,9 @@ int64_t prefill_grid_size(const PrefillArgs& a);
 // Enqueue the kernel; returns the launch's hipError_t.
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
-// The same two calls at head_dim 128 (packed K/V only: the grid size is -1
-// for a paged cache).
-int64_t prefill_grid_size_d128(const PrefillArgs& a);
-hipError_t launch_prefill_d128(const PrefillArgs& a, hipStream_t stream);
+// The same two calls for the 128-row work-groups of prefill_fwd_narrow.hip, at
+// head_dim 64 or 128 (packed K/V only: the grid size is -1 for a paged cache).
+int64_t prefill_grid_size_narrow(const PrefillArgs& a, int head_dim);
+hipError_t launch_prefill_narrow(const PrefillArgs& a, int head_dim, hipStream_t stream);
 
 }  // namespace tsmha

@@ -1,35 +1,42 @@
-// prefill_fwd_d128.hip -- gfx950 (CDNA4) kernels for causal grouped-query
-// prefill attention with sliding windows and attention sinks at head_dim 128.
+// prefill_fwd_narrow.hip -- gfx950 (CDNA4) kernels for causal grouped-query
+// prefill attention with sliding windows and attention sinks, 32 query rows
+// per wave: head_dim 128, and head_dim 64 when the launch is too small to fill
+// the GPU with the 256-row work-groups of prefill_fwd.hip.
 //
 // The same operation as the head_dim 64 kernels (the `mha_prefill` call of the
 // TokenSpeed-kernel README, section "Public API"; sinks and sliding windows as
 // for the GPT-OSS layers of "TokenSpeed-kernel multi-silicon", section
-// "Числа: Gluon на AMD MI355X"), for the other head width the README's kernel
-// traits name.  The design follows the head_dim 64 kernel, resized:
+// "Числа: Gluon на AMD MI355X"); head_dim 128 is the other head width the
+// README's kernel traits name.  The design follows the head_dim 64 kernel of
+// prefill_fwd.hip, resized:
 //
 // Work decomposition.  One work-group (4 waves) owns 128 query rows: all G
 // query heads of one KV head for P = 128 / G consecutive positions of one
-// sequence; each wave holds 32 of them, so that the output (128 x 32 fp32)
-// and the query operand (32 x 128 bf16) take the registers the head_dim 64
-// kernel spends on 64 rows.  Every K/V tile staged in LDS serves the whole
-// head group.
+// sequence; each wave holds 32 of them, so that at head_dim 128 the output
+// (128 x 32 fp32) and the query operand (32 x 128 bf16) take the registers the
+// head_dim 64 kernel spends on 64 rows.  At head_dim 64 the same shape needs
+// about 145 VGPRs and 32 KiB of LDS, so three work-groups fit on a compute
+// unit, and a launch has twice as many work-groups, each with half the rows:
+// that fills the GPU on short or few sequences.  Every K/V tile staged in LDS
+// serves the whole head group.
 //
 // Orientation.  Scores are formed transposed, S^T = K Q^T, with
-// v_mfma_f32_32x32x16_bf16 (two 32-key blocks per 64-key tile, eight 16-wide
-// steps of head_dim); lane l holds query l % 32.  The output is accumulated
-// transposed too, O^T += V^T P^T (four 32-row blocks of head_dim), with V^T
-// read by ds_read_b64_tr_b16 from the row-major V tile and P^T taken straight
-// from the score accumulators.
+// v_mfma_f32_32x32x16_bf16 (two 32-key blocks per 64-key tile, D / 16 steps of
+// head_dim); lane l holds query l % 32.  The output is accumulated transposed
+// too, O^T += V^T P^T (D / 32 blocks of 32 head_dim rows), with V^T read by
+// ds_read_b64_tr_b16 from the row-major V tile and P^T taken straight from the
+// score accumulators.
 //
-// Staging.  K and V tiles (64 rows of 256 bytes) move from HBM to LDS with
+// Staging.  K and V tiles (64 rows of 2 D bytes) move from HBM to LDS with
 // buffer_load_dwordx4 ... lds, double-buffered; the query rows are staged once
-// in the second slot before the walk, so the work-group uses 64 KiB of LDS and
-// two fit on a compute unit.  A 16-byte chunk c of row r sits at position
+// in the second slot before the walk (64 KiB of LDS per work-group at head_dim
+// 128, 32 KiB at 64).  A 16-byte chunk c of a 256-byte row r sits at position
 // c ^ (((r & 3) << 2) | ((r >> 2) & 3)): 16 consecutive rows reading one chunk
 // (K and Q operands) and 4 aligned rows reading two adjacent chunks (the
-// transposed V reads) each hit distinct banks of the 64-bank LDS.
+// transposed V reads) each hit distinct banks of the 64-bank LDS; 128-byte
+// rows use the swizzle of cdna4.h, laid out for the same access patterns.
 //
-// Softmax.  As at head_dim 64: base 2, scale * log2(e) folded into the bf16
+// Softmax.  As in prefill_fwd.hip: base 2, scale * log2(e) folded into the bf16
 // query operand, every probability exp2 of its score against reference 1,
 // row sums on the matrix pipe, and a streaming softmax with running maxima for
 // a work-group whose sums leave [2^-64, 2^65).
@@ -48,16 +55,23 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kD = 128;                        // head_dim
 constexpr int kBK = 64;                        // keys per LDS tile
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQW = 32;                        // query rows per wave
 constexpr int kRows = kQW * kWaves;            // (query head, position) rows per work-group
-constexpr int kRowBytes = kD * 2;              // one K, V or Q row in bytes
-constexpr int kChunks = kRowBytes / 16;        // 16-byte chunks per row
-constexpr int kTileBytes = kBK * kRowBytes;    // 16 KiB
-constexpr int kTileChunks = kTileBytes / 16;
+template <int D>
+struct Shape {
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kChunks = kRowBytes / 16;
+  static constexpr int kTileBytes = kBK * kRowBytes;
+  static constexpr int kTileChunks = kTileBytes / 16;
+  static constexpr int kKS = D / 16;
+  static constexpr int kDB = D / 32;
+  static constexpr int kRPL = 1024 / kRowBytes;       // rows per wave-wide 1 KiB load
+  static constexpr int kTileLoads = 16 / kRPL;         // a wave's loads per tile and tensor
+  static constexpr int kQLoads = kQW / kRPL;           // a wave's loads of its query rows
+};
 constexpr int kFastSumBinades = 64;  // the fast pass keeps row sums in [2^-64, 2^65)
 constexpr int kMaskCausal = 1;       // mask kinds: key past the row's position
 constexpr int kMaskWindow = 2;       // ... key before the row's window
@@ -78,7 +92,12 @@ struct Params {
 
 // Position of 16-byte chunk `ch` of row `row` in a tile of 256-byte rows.
 __device__ __forceinline__ int key16(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
-__device__ __forceinline__ int pos16(int row, int ch) { return row * kChunks + (ch ^ key16(row)); }
+template <int D>
+__device__ __forceinline__ int tkey(int row) {
+  if constexpr (D == 128) return key16(row); else return swz_key(row);
+}
+template <int D>
+__device__ __forceinline__ int tpos(int row, int ch) { return row * Shape<D>::kChunks + (ch ^ tkey<D>(row)); }
 
 __device__ __forceinline__ float pair_max(float x) {
   const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -98,8 +117,17 @@ __device__ __forceinline__ float max16(const f32x16& a) {
   return fmaxf(fmaxf(x, a[14]), fmaxf(y, a[15]));
 }
 
-template <int G, bool WINDOWED>
-__global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
+template <int D, int G, bool WINDOWED>
+__global__ void __launch_bounds__(kThreads, D == 64 ? 3 : 2) prefill_fwd_narrow(Params p) {
+  using S = Shape<D>;
+  constexpr int kD = D;
+  constexpr int kRowBytes = S::kRowBytes;
+  constexpr int kChunks = S::kChunks;
+  constexpr int kTileBytes = S::kTileBytes;
+  constexpr int kTileChunks = S::kTileChunks;
+  constexpr int KS = S::kKS;
+  constexpr int DB = S::kDB;
+  constexpr int RPL = S::kRPL;
   constexpr int P = kRows / G;  // positions per work-group
   __shared__ u32x4 lds_k[2 * kTileChunks];
   __shared__ u32x4 lds_v[2 * kTileChunks];
@@ -143,18 +171,18 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
   const int tile_stride = kBK * Hkv * kRowBytes;
   const i32x4 rk = buffer_rsrc(p.k + seq_elems, nbytes);
   const i32x4 rv = buffer_rsrc(p.v + seq_elems, nbytes);
-  int voff[4];
+  int voff[S::kTileLoads];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 16 * w + 4 * i + (lane >> 4);
-    voff[i] = (row * Hkv + g) * kRowBytes + ((lane & 15) ^ key16(row)) * 16;
+  for (int i = 0; i < S::kTileLoads; ++i) {
+    const int row = 16 * w + RPL * i + lane / kChunks;
+    voff[i] = (row * Hkv + g) * kRowBytes + ((lane % kChunks) ^ tkey<D>(row)) * 16;
   }
   const uint32_t lds_k_base = lds_addr(lds_k) + w * 16 * kRowBytes;
   const uint32_t lds_v_base = lds_addr(lds_v) + w * 16 * kRowBytes;
   auto issue_tile = [&](int t, int buf) {
     const int off = t * tile_stride;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < S::kTileLoads; ++i) {
       lds_dma16(lds_k_base + buf * kTileBytes + i * 1024, rk, off + voff[i]);
       lds_dma16(lds_v_base + buf * kTileBytes + i * 1024, rv, off + voff[i]);
     }
@@ -180,24 +208,24 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
   {
     const i32x4 rq = buffer_rsrc(p.q + (int64_t)s * Hq * kD, L * Hq * kRowBytes);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = 4 * i + (lane >> 4);  // within the wave's 32 rows
+    for (int i = 0; i < S::kQLoads; ++i) {
+      const int row = RPL * i + lane / kChunks;  // within the wave's 32 rows
       const int r = kQW * w + row;
-      const int data_ch = (lane & 15) ^ key16(row);
+      const int data_ch = (lane % kChunks) ^ tkey<D>(row);
       lds_dma16(q_lds + i * 1024, rq, ((p0 + r / G) * Hq + g * G + r % G) * kRowBytes + data_ch * 16);
     }
   }
   issue_tile(kt1, 0);
-  wait_vmem<8>();  // the query rows have landed (loads complete in order; the tile's 8 may not)
+  wait_vmem<2 * S::kTileLoads>();  // the query rows have landed (the tile's loads may not)
   // Query operand (B of the score MFMA) for the eight 16-wide steps of
   // head_dim: lane l holds elements 16 ks + 8 hi .. + 7 of its row, times
   // scale * log2(e), rounded once to bf16.
-  bf16x8 qf[8];
+  bf16x8 qf[KS];
   {
     const lds_char* qb = (w < 2 ? (const lds_char*)lds_k : (const lds_char*)lds_v) + kTileBytes + (w & 1) * kQW * kRowBytes;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 x = *(const bf16x8*)(qb + pos16(l32, 2 * ks + hi) * 16);
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 x = *(const bf16x8*)(qb + tpos<D>(l32, 2 * ks + hi) * 16);
 #pragma unroll
       for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)((float)x[e] * c);
     }
@@ -206,20 +234,20 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
   // Per-lane byte offsets of the operand reads within a tile, fixed for the
   // walk: K rows 32 mb + l32 share their swizzle with row l32, and the V rows
   // of PV step s4 with step 0, so the key half and the step add immediates.
-  uint32_t koff[8], vlo_off[4], vhi_off[4];
+  uint32_t koff[KS], vlo_off[DB], vhi_off[DB];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) koff[ks] = (uint32_t)(pos16(l32, 2 * ks + hi) * 16);
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = (uint32_t)(tpos<D>(l32, 2 * ks + hi) * 16);
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
+  for (int db = 0; db < DB; ++db) {
     const int key_lo = 4 * hi + (r16 >> 2);
     const int key_hi = key_lo + 8;
     const int d = 32 * db + 16 * half16 + 4 * (r16 & 3);
-    vlo_off[db] = (uint32_t)(pos16(key_lo, d >> 3) * 16 + (d & 7) * 2);
-    vhi_off[db] = (uint32_t)(pos16(key_hi, d >> 3) * 16 + (d & 7) * 2);
+    vlo_off[db] = (uint32_t)(tpos<D>(key_lo, d >> 3) * 16 + (d & 7) * 2);
+    vhi_off[db] = (uint32_t)(tpos<D>(key_hi, d >> 3) * 16 + (d & 7) * 2);
   }
-  auto read_k = [&](const lds_char* kl, int mb, bf16x8 (&ka)[8]) {
+  auto read_k = [&](const lds_char* kl, int mb, bf16x8 (&ka)[KS]) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) ka[ks] = *(const bf16x8*)(kl + mb * 32 * kRowBytes + koff[ks]);
+    for (int ks = 0; ks < KS; ++ks) ka[ks] = *(const bf16x8*)(kl + mb * 32 * kRowBytes + koff[ks]);
   };
   // V^T fragment (A of the PV MFMA) of PV step s4 (keys 16 s4 .. +15) and head_dim block db.
   auto read_v = [&](const lds_char* vb, int s4, int db) -> bf16x8 {
@@ -232,7 +260,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
   // Scores of key half mb: element e holds key k0 + 32 mb + 8 (e / 4) + 4 hi + e % 4.
   // Masked tiles start the accumulator from the mask (0 visible, -inf hidden).
   // Mask kinds: 0 none, 1 causal only, 2 window only, 3 both.
-  auto qk = [&](auto mask_tag, const bf16x8 (&ka)[8], int mb, int k0) -> f32x16 {
+  auto qk = [&](auto mask_tag, const bf16x8 (&ka)[KS], int mb, int k0) -> f32x16 {
     constexpr int M = decltype(mask_tag)::value;
     static_assert(WINDOWED || (M & kMaskWindow) == 0, "window mask without a window");
     f32x16 acc = {};
@@ -253,7 +281,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
       }
     }
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], acc, 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], acc, 0, 0, 0);
     return acc;
   };
   // bf16 P^T of one score block in the PV B-operand order (plo: PV step 2 mb,
@@ -282,22 +310,22 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
   const int lsel = ((lane & 15) == 0 && ((lane >> 4) & 1) == 0) || ((lane & 15) == 1 && ((lane >> 4) & 1) == 1);
   const bf16x8 sel = __builtin_bit_cast(bf16x8, lsel ? u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u}
                                                      : u32x4{0u, 0u, 0u, 0u});
-  f32x16 o[4];  // O^T blocks: head_dim 32 db .. + 31 x the wave's 32 queries
+  f32x16 o[DB];  // O^T blocks: head_dim 32 db .. + 31 x the wave's 32 queries
   f32x4 lacc;
   float mref, lsum;
   // V^T fragments of PV steps s0, s0 + 1 (all four head_dim blocks), and
   // O^T += V^T P^T over them.
-  auto read_v2 = [&](const lds_char* vb, int s0, bf16x8 (&va)[2][4]) {
+  auto read_v2 = [&](const lds_char* vb, int s0, bf16x8 (&va)[2][DB]) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) va[j][db] = read_v(vb, s0 + j, db);
+      for (int db = 0; db < DB; ++db) va[j][db] = read_v(vb, s0 + j, db);
   };
-  auto pv2 = [&](const bf16x8 (&va)[2][4], const bf16x8 (&pf)[4], int s0) {
+  auto pv2 = [&](const bf16x8 (&va)[2][DB], const bf16x8 (&pf)[4], int s0) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < DB; ++db)
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j][db], pf[s0 + j], o[db], 0, 0, 0);
   };
   auto interleave = [](auto k_tag, auto n_tag) {
@@ -317,7 +345,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
   // a time, which leaves the compiler room to keep the K reads ahead of the
   // score MFMAs).
   auto tile_fast = [&](auto mask_tag, const lds_char* kl, const lds_char* vb, int k0) {
-    bf16x8 ka[8], pf[4], va[4], vn[4];
+    bf16x8 ka[KS], pf[4], va[DB], vn[DB];
     read_k(kl, 0, ka);
     const f32x16 s0 = qk(mask_tag, ka, 0, k0);
     __builtin_amdgcn_sched_barrier(0);
@@ -325,25 +353,25 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
     const f32x16 s1 = qk(mask_tag, ka, 1, k0);
     probs(s0, 0.f, pf[0], pf[1]);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) va[db] = read_v(vb, 0, db);
-    interleave(std::integral_constant<int, 8>{}, std::integral_constant<int, 3>{});
+    for (int db = 0; db < DB; ++db) va[db] = read_v(vb, 0, db);
+    interleave(std::integral_constant<int, KS>{}, std::integral_constant<int, 24 / KS>{});
     __builtin_amdgcn_sched_barrier(0);
-    auto pv_step = [&](const bf16x8 (&v)[4], const bf16x8& pfrag) {
+    auto pv_step = [&](const bf16x8 (&v)[DB], const bf16x8& pfrag) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[db], pfrag, o[db], 0, 0, 0);
+      for (int db = 0; db < DB; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[db], pfrag, o[db], 0, 0, 0);
       lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pfrag, lacc, 0, 0, 0);
     };
 #pragma unroll
-    for (int db = 0; db < 4; ++db) vn[db] = read_v(vb, 1, db);
+    for (int db = 0; db < DB; ++db) vn[db] = read_v(vb, 1, db);
     pv_step(va, pf[0]);
     probs(s1, 0.f, pf[2], pf[3]);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) va[db] = read_v(vb, 2, db);
+    for (int db = 0; db < DB; ++db) va[db] = read_v(vb, 2, db);
     pv_step(vn, pf[1]);
-    interleave(std::integral_constant<int, 10>{}, std::integral_constant<int, 3>{});
+    interleave(std::integral_constant<int, 2 * (DB + 1)>{}, std::integral_constant<int, (24 + 2 * DB + 1) / (2 * (DB + 1))>{});
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) vn[db] = read_v(vb, 3, db);
+    for (int db = 0; db < DB; ++db) vn[db] = read_v(vb, 3, db);
     pv_step(va, pf[2]);
     pv_step(vn, pf[3]);
   };
@@ -352,7 +380,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
   // row's window).
   auto tile_half = [&](auto mb_tag, auto mask_tag, const lds_char* kl, const lds_char* vb, int k0) {
     constexpr int mb = decltype(mb_tag)::value;
-    bf16x8 ka[8], pf[4], va[2][4];
+    bf16x8 ka[KS], pf[4], va[2][DB];
     read_k(kl, mb, ka);
     const f32x16 sc = qk(mask_tag, ka, mb, k0);
     __builtin_amdgcn_sched_barrier(0);
@@ -368,7 +396,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
   auto tile_exact = [&](const lds_char* kl, const lds_char* vb, int k0) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      bf16x8 ka[8], pf[4];
+      bf16x8 ka[KS], pf[4];
       read_k(kl, mb, ka);
       const f32x16 sc = qk(std::integral_constant<int, kMaskCausal | (WINDOWED ? kMaskWindow : 0)>{}, ka, mb, k0);
       const float mx = pair_max(max16(sc));
@@ -376,14 +404,14 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
         const float alpha = __builtin_amdgcn_exp2f(mref - mx);
         lsum *= alpha;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
         mref = mx;
       }
       const float m = (mref == -INFINITY) ? 0.f : mref;
       lsum += probs_sum(sc, m, pf[2 * mb], pf[2 * mb + 1]);
-      bf16x8 va[2][4];
+      bf16x8 va[2][DB];
       read_v2(vb, 2 * mb, va);
       pv2(va, pf, 2 * mb);
     }
@@ -423,7 +451,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
     lsum = 0.f;
     lacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
   };
@@ -468,7 +496,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
   {
     float osum = 0.f;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) osum += o[db][e];
     const bool bad = !positive_in_binade_range(lrow, -kFastSumBinades, kFastSumBinades) || !finite_bits(osum);
@@ -502,37 +530,48 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d128(Params p) {
   if (p.sinks) lt += __builtin_amdgcn_exp2f(sink_t() - mref);
   const float inv = 1.f / lt;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int vg = 0; vg < 4; ++vg) {
       // head_dim elements 32 db + 8 vg + 4 hi .. + 3: half hi of chunk 4 db + vg
       bf16x4 val;
 #pragma unroll
       for (int e = 0; e < 4; ++e) val[e] = (__bf16)(o[db][4 * vg + e] * inv);
-      *(u32x2*)(ob + pos16(el32, 4 * db + vg) * 16 + 8 * ehi) = __builtin_bit_cast(u32x2, val);
+      *(u32x2*)(ob + tpos<D>(el32, 4 * db + vg) * 16 + 8 * ehi) = __builtin_bit_cast(u32x2, val);
     }
   {
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(p.out + (int64_t)s * Hq * kD), 0, L * Hq * kRowBytes, kBufferConfig);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = 4 * i + (el >> 4);  // within the wave's 32 rows
+    for (int i = 0; i < S::kQLoads; ++i) {
+      const int row = RPL * i + el / kChunks;  // within the wave's 32 rows
       const int r = kQW * w + row;
-      const int ch = el & 15;
-      const u32x4 x = *(const u32x4*)(ob + pos16(row, ch) * 16);
+      const int ch = el % kChunks;
+      const u32x4 x = *(const u32x4*)(ob + tpos<D>(row, ch) * 16);
       __builtin_amdgcn_raw_buffer_store_b128(x, ro, ((p0 + r / G) * Hq + g * G + r % G) * kRowBytes + ch * 16, 0, 0);
     }
   }
 }
 
-template <int G>
+template <int D, int G>
 hipError_t launch_g(const Params& kp, int64_t grid, bool windowed, hipStream_t stream) {
   const dim3 gd((unsigned)grid), bd(kThreads);
   if (windowed)
-    hipLaunchKernelGGL((prefill_fwd_d128<G, true>), gd, bd, 0, stream, kp);
+    hipLaunchKernelGGL((prefill_fwd_narrow<D, G, true>), gd, bd, 0, stream, kp);
   else
-    hipLaunchKernelGGL((prefill_fwd_d128<G, false>), gd, bd, 0, stream, kp);
+    hipLaunchKernelGGL((prefill_fwd_narrow<D, G, false>), gd, bd, 0, stream, kp);
   return hipGetLastError();
+}
+template <int D>
+hipError_t launch_d(const Params& kp, int64_t grid, int G, bool windowed, hipStream_t stream) {
+  switch (G) {
+    case 1: return launch_g<D, 1>(kp, grid, windowed, stream);
+    case 2: return launch_g<D, 2>(kp, grid, windowed, stream);
+    case 4: return launch_g<D, 4>(kp, grid, windowed, stream);
+    case 8: return launch_g<D, 8>(kp, grid, windowed, stream);
+    case 16: return launch_g<D, 16>(kp, grid, windowed, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 int64_t pblocks128(const PrefillArgs& a) {
@@ -542,17 +581,18 @@ int64_t pblocks128(const PrefillArgs& a) {
 
 }  // namespace
 
-int64_t prefill_grid_size_d128(const PrefillArgs& a) {
-  if (a.block_table) return -1;  // no paged form at this width
-  if (((int64_t)a.max_seqlen + kBK) * a.n_kv_heads * kRowBytes > 0x7fffffffLL) return -1;
-  if (((int64_t)a.max_seqlen + kRows) * a.n_q_heads * kRowBytes > 0x7fffffffLL) return -1;
+int64_t prefill_grid_size_narrow(const PrefillArgs& a, int head_dim) {
+  if (a.block_table) return -1;  // no paged form
+  const int64_t row_bytes = 2 * (int64_t)head_dim;
+  if (((int64_t)a.max_seqlen + kBK) * a.n_kv_heads * row_bytes > 0x7fffffffLL) return -1;
+  if (((int64_t)a.max_seqlen + kRows) * a.n_q_heads * row_bytes > 0x7fffffffLL) return -1;
   const int64_t n = pblocks128(a) * (int64_t)a.n_seqs * (int64_t)a.n_kv_heads;
   if (n > 0x7fffffffLL) return -1;
   return n;
 }
 
-hipError_t launch_prefill_d128(const PrefillArgs& a, hipStream_t stream) {
-  const int64_t grid = prefill_grid_size_d128(a);
+hipError_t launch_prefill_narrow(const PrefillArgs& a, int head_dim, hipStream_t stream) {
+  const int64_t grid = prefill_grid_size_narrow(a, head_dim);
   if (grid <= 0) return hipSuccess;
   Params kp;
   kp.q = static_cast<const uint16_t*>(a.q);
@@ -568,14 +608,8 @@ hipError_t launch_prefill_d128(const PrefillArgs& a, hipStream_t stream) {
   kp.c = (float)((double)a.softmax_scale * 1.4426950408889634);
   const bool windowed = a.window > 0;
   (void)hipGetLastError();
-  switch (a.n_q_heads / a.n_kv_heads) {
-    case 1: return launch_g<1>(kp, grid, windowed, stream);
-    case 2: return launch_g<2>(kp, grid, windowed, stream);
-    case 4: return launch_g<4>(kp, grid, windowed, stream);
-    case 8: return launch_g<8>(kp, grid, windowed, stream);
-    case 16: return launch_g<16>(kp, grid, windowed, stream);
-    default: return hipErrorInvalidValue;
-  }
+  const int G = a.n_q_heads / a.n_kv_heads;
+  return head_dim == 128 ? launch_d<128>(kp, grid, G, windowed, stream) : launch_d<64>(kp, grid, G, windowed, stream);
 }
 
 }  // namespace tsmha

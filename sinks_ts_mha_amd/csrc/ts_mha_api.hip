@@ -21,15 +21,19 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 
-// Per-device answer to "is this a gfx950?": 0 unknown, 1 yes, 2 no.
+// Per-device answer to "is this a gfx950?": 0 unknown, 1 yes, 2 no; and its
+// number of compute units.
 int g_arch_state[kMaxDevices];
+int g_cu_count[kMaxDevices];
+constexpr int kDefaultCUs = 256;  // MI355X, when the device was not queried (test hook)
 std::mutex g_arch_mutex;
 
 thread_local char g_launch_msg[256] = "";
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-int check_device() {
+int check_device(int* cus = nullptr) {
+  if (cus) *cus = kDefaultCUs;
   int count = 0;
   if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
     (void)hipGetLastError();
@@ -52,7 +56,9 @@ int check_device() {
       return TS_MHA_ERR_NO_DEVICE;
     }
     g_arch_state[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_cu_count[dev] = prop.multiProcessorCount;
   }
+  if (cus && g_cu_count[dev] > 0) *cus = g_cu_count[dev];
   return g_arch_state[dev] == 1 ? TS_MHA_OK : TS_MHA_ERR_ARCH;
 }
 
@@ -176,11 +182,27 @@ extern "C" int ts_mha_prefill(const void* q, const void* k, const void* v, const
   a.softmax_scale = softmax_scale;
   a.n_seqs = n_seqs;
   a.max_seqlen = max_seqlen;
-  const int64_t grid = head_dim == 128 ? tsmha::prefill_grid_size_d128(a) : tsmha::prefill_grid_size(a);
-  if (grid < 0) return TS_MHA_ERR_BAD_SHAPE;
+  // head_dim 64 has two kernels: the 256-row work-groups of prefill_fwd.hip,
+  // and the 128-row ones of prefill_fwd_narrow.hip, which take over when the
+  // former would give no compute unit more than two work-groups (short or few
+  // sequences): twice as many work-groups, each half as long, then fill the
+  // GPU.  head_dim 128 always uses the 128-row form.  TS_MHA_PREFILL_KERNEL =
+  // wide | narrow forces one of the head_dim 64 kernels (tests, measurement).
+  const int64_t wide = head_dim == 64 ? tsmha::prefill_grid_size(a) : -1;
+  const int64_t narrow = tsmha::prefill_grid_size_narrow(a, head_dim);
+  if ((head_dim == 64 ? wide : narrow) < 0) return TS_MHA_ERR_BAD_SHAPE;
 
-  const int dev_rc = check_device();
+  int cus = 0;
+  const int dev_rc = check_device(&cus);
   if (dev_rc != TS_MHA_OK) return dev_rc;
+  bool use_narrow = true;
+  if (head_dim == 64) {
+    const char* kname = getenv("TS_MHA_PREFILL_KERNEL");
+    if (kname && strcmp(kname, "wide") == 0) use_narrow = false;
+    else if (kname && strcmp(kname, "narrow") == 0) use_narrow = narrow >= 0;
+    else use_narrow = narrow >= 0 && wide <= 2 * (int64_t)cus;
+  }
+  const int64_t grid = use_narrow ? narrow : wide;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const char* dbg = getenv("TS_MHA_VALIDATE");
@@ -190,7 +212,7 @@ extern "C" int ts_mha_prefill(const void* q, const void* k, const void* v, const
   }
   if (grid == 0) return TS_MHA_OK;
 
-  const hipError_t err = head_dim == 128 ? tsmha::launch_prefill_d128(a, st) : tsmha::launch_prefill(a, st);
+  const hipError_t err = use_narrow ? tsmha::launch_prefill_narrow(a, head_dim, st) : tsmha::launch_prefill(a, st);
   if (err != hipSuccess) {
     snprintf(g_launch_msg, sizeof g_launch_msg, "%s", hipGetErrorString(err));
     return TS_MHA_ERR_LAUNCH;

@@ -47,14 +47,17 @@ SMALL_CASES = [
 ]
 
 
+@pytest.mark.parametrize("kernel", ["wide", "narrow"])
 @pytest.mark.parametrize("case", SMALL_CASES, ids=[f"c{n}" for n in range(len(SMALL_CASES))])
-def test_small_parity(case, oracle_lib):
+def test_small_parity(case, kernel, oracle_lib, monkeypatch):
+    """Both head_dim 64 kernels (256- and 128-row work-groups), forced."""
+    monkeypatch.setenv("TS_MHA_PREFILL_KERNEL", kernel)
     seqlens, hq, hkv, w, sinks = case
     wl = workloads.custom(seqlens, hq, hkv, window=w, sinks=sinks, seed=7)
     inp = workloads.make_inputs(wl)
     if sinks:
         inp["sinks"] = inp["sinks"] * 2.0  # wider spread of sink weights
-    say(f"small parity seqlens={seqlens} Hq={hq} Hkv={hkv} W={w} sinks={sinks}")
+    say(f"small parity ({kernel}) seqlens={seqlens} Hq={hq} Hkv={hkv} W={w} sinks={sinks}")
     got = f64(run_gpu(inp).cpu())
     torch.cuda.synchronize()
     ref = oracle.prefill(*oracle_args(inp), lib=oracle_lib)

@@ -109,16 +109,18 @@ def test_sink_values(sink, oracle_lib):
         assert np.max(np.abs(got)) < 1e-6
 
 
+@pytest.mark.parametrize("kernel", ["wide", "narrow"])
 @pytest.mark.parametrize("seed", [6, 19])
 @pytest.mark.parametrize("window", [0, 100])
 @pytest.mark.parametrize("with_sinks", [True, False], ids=["sinks", "nosinks"])
-def test_wide_logit_range(window, with_sinks, seed, oracle_lib):
+def test_wide_logit_range(window, with_sinks, seed, kernel, oracle_lib, monkeypatch):
     """Queries scaled by 40 spread each row's logits over hundreds of log2 units,
     so measured against the row's own key many probabilities overflow fp32 (or
     their sums pass 2^64) in the fast pass.  Those work-groups must redo their
     rows with running maxima; every row still meets the rounding bound.  With seed
     19 some work-groups' row sums come out NaN (an infinite probability times a
     zero of the row-sum selector): the range test must catch NaN too."""
+    monkeypatch.setenv("TS_MHA_PREFILL_KERNEL", kernel)
     wl = workloads.custom([700, 333, 64, 5], 16, 2, window=window, seed=seed)
     inp = workloads.make_inputs(wl)
     inp["q"] = (inp["q"].to(torch.float32) * 40.0).to(torch.bfloat16)
@@ -173,6 +175,25 @@ def test_packed_equals_alone_bitwise():
                    cu_seqlens=torch.tensor([0, e - s], dtype=torch.int32), max_seqlen=e - s)
         alone = run_gpu(one).cpu()
         assert torch.equal(alone.view(torch.int16), packed[s:e].view(torch.int16)), f"sequence {b}"
+
+
+@pytest.mark.parametrize("shape", [([70, 1, 300, 129, 0, 64], 16, 2, 100), ([1000, 333], 64, 8, 0),
+                                   ([2048] * 2, 64, 8, 128), ([517, 65, 1], 32, 2, 0), ([300], 8, 8, 0)],
+                         ids=["ragged_w100", "g8", "g8_w128", "g16", "g1"])
+def test_wide_and_narrow_kernels_agree_bitwise(shape, monkeypatch):
+    """At head_dim 64 the launch picks the 256- or the 128-row work-groups by grid
+    size; for each row both walk its visible keys with the same instructions in the
+    same order (the extra keys either kind covers are masked or skipped and add exact
+    zeros), so their outputs are identical bit for bit."""
+    seqlens, hq, hkv, w = shape
+    wl = workloads.custom(seqlens, hq, hkv, window=w, seed=12)
+    inp = workloads.make_inputs(wl)
+    say(f"wide vs narrow {shape}")
+    monkeypatch.setenv("TS_MHA_PREFILL_KERNEL", "wide")
+    a = run_gpu(inp).cpu()
+    monkeypatch.setenv("TS_MHA_PREFILL_KERNEL", "narrow")
+    b = run_gpu(inp).cpu()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
 def test_deterministic_bitwise():
