@@ -29,6 +29,13 @@ read once, q read, out written).  `value` uses the wall time of eager calls
 (host overhead included); `gpu_avg_us` and `frac_hbm` (against the 8 TB/s roof)
 use the same calls replayed from one captured HIP graph.
 
+--sweep times the chart family (full causal, 64/8 heads, head_dim 64, batch x
+seq_len): `kernel_avg_us` and `frac` from the eager launches' event pair (on the
+smallest points the host's per-call overhead exceeds the kernel and shows up as
+gaps), `graph_avg_us` and `frac_graph` from the same launches replayed from one
+captured HIP graph (no host call per launch, but the graph's own gap between
+nodes, a few microseconds).  A kernel trace gives the kernel's own duration.
+
 --prefill-kvcache times ts_mha_prefill_with_kvcache (chunked prefill: new rows at
 the end of each sequence's cached keys) and reports TFLOP/s over the visible
 (query, key) pairs, as the main metric does, against the bf16 MFMA peak.
@@ -253,9 +260,10 @@ def main():
             torch.cuda.synchronize()
         return n
 
-    def timed(wl, steps, warmup, copy_calibration=False):
+    def timed(wl, steps, warmup, copy_calibration=False, graph_replay=False):
         """Resident inputs, W warm-up launches, then K launches timed on the host clock and by
-        one pair of HIP events on the launch stream: (inputs, ms per step, kernel avg ms)."""
+        one pair of HIP events on the launch stream: (inputs, ms per step, kernel avg ms,
+        graph-replay avg ms or None)."""
         inp = workloads.make_inputs(wl)
         q, k, v = inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev)
         sinks = inp["sinks"].to(dev) if inp["sinks"] is not None else None
@@ -287,8 +295,34 @@ def main():
         ev1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        ms_graph = None
+        if graph_replay:
+            # The same K launches captured in one HIP graph, replayed between one pair of
+            # events on the replay stream: GPU time without the host's per-call overhead
+            # (which on the smallest workloads exceeds the kernel's own duration), with the
+            # graph's own gap between nodes instead.
+            graph = torch.cuda.CUDAGraph()
+            gs = torch.cuda.Stream()
+            gs.wait_stream(stream)
+            with torch.cuda.stream(gs):
+                with torch.cuda.graph(graph, stream=gs):
+                    for _ in range(steps):
+                        tm.ts_mha_prefill(q, k, v, sinks, cu, window=wl.window,
+                                          softmax_scale=wl.softmax_scale, out=out,
+                                          max_seqlen=wl.max_seqlen)
+            g0 = torch.cuda.Event(enable_timing=True)
+            g1 = torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(gs):
+                graph.replay()
+                torch.cuda.synchronize()
+                g0.record(gs)
+                graph.replay()
+                g1.record(gs)
+            torch.cuda.synchronize()
+            ms_graph = g0.elapsed_time(g1) / steps
+            del graph
         del q, k, v, sinks, cu, out
-        return inp, wall * 1e3 / steps, ev0.elapsed_time(ev1) / steps
+        return inp, wall * 1e3 / steps, ev0.elapsed_time(ev1) / steps, ms_graph
 
     if a.prefill_kvcache:
         for name, wl in workloads.PREFILL_KV_WORKLOADS.items():
@@ -395,12 +429,14 @@ def main():
 
     if a.sweep:
         for wl in workloads.SWEEP.values():
-            _, ms_step, ms_kernel = timed(wl, a.steps, a.warmup)
+            _, ms_step, ms_kernel, ms_graph = timed(wl, a.steps, a.warmup, graph_replay=True)
             flops = 4 * wl.head_dim * wl.n_q_heads * tm.ts_mha_unmasked_pairs(wl.cu_seqlens(), 0)
             print(json.dumps({"sweep_point": wl.name, "batch": len(wl.seqlens), "seq_len": wl.seqlens[0],
                               "value": round(flops / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
                               "kernel_avg_us": round(ms_kernel * 1e3, 2),
                               "frac": round(flops / (ms_kernel * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                              "graph_avg_us": round(ms_graph * 1e3, 2),
+                              "frac_graph": round(flops / (ms_graph * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                               "steps": a.steps, "warmup": a.warmup,
                               "warmup_launches": warm_counts[wl.name]}), flush=True)
             torch.cuda.empty_cache()
@@ -408,7 +444,7 @@ def main():
 
     name = a.workload or workloads.DEFAULT_BENCH_WORKLOAD
     wl = workloads.get(name)
-    inp, ms_per_step, avg_ms = timed(wl, a.steps, a.warmup, a.copy_calibration)
+    inp, ms_per_step, avg_ms, _ = timed(wl, a.steps, a.warmup, a.copy_calibration)
 
     pairs = tm.ts_mha_unmasked_pairs(wl.cu_seqlens(), wl.window)
     flops = 4 * wl.head_dim * wl.n_q_heads * pairs
