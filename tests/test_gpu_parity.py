@@ -96,13 +96,16 @@ def test_long_prefill_sampled_rows(oracle_lib):
     check(got[rows, heads], ref, "long_1x32768 sampled")
 
 
-SWEEP_CASES = ["sweep_b16_s1024", "sweep_b2_s4096", "sweep_b1_s8192", "sweep_b16_s8192"]
+# 1x1K, 2x1K and 1x2K run the 128-row kernel (their 256-row grids would leave CU slots empty)
+SWEEP_CASES = ["sweep_b1_s1024", "sweep_b2_s1024", "sweep_b1_s2048", "sweep_b16_s1024",
+               "sweep_b2_s4096", "sweep_b1_s8192", "sweep_b16_s8192"]
 
 
 @pytest.mark.parametrize("name", SWEEP_CASES)
 def test_chart_point_sampled_rows(name, oracle_lib):
-    """Points of the chart family (sequence length x batch, full causal), at their real sizes:
-    in every sequence the first 64 positions, the last 32 and every 257th, every query head."""
+    """Points of the chart family (sequence length x batch, full causal), at their real sizes
+    and with the kernel the call picks for them: in every sequence the first 64 positions,
+    the last 32 and every 257th, every query head."""
     wl = workloads.get(name)
     inp = workloads.make_inputs(wl)
     say(f"chart point {name} T={wl.total_tokens}")
