@@ -72,6 +72,24 @@ def test_workload_parity_all_rows_d128(name, oracle_lib):
     gate(got, oracle.prefill(*oracle_args(inp), lib=oracle_lib), name)
 
 
+@pytest.mark.parametrize("window", [0, 128])
+def test_long_sequence_sampled_rows_d128(window, oracle_lib):
+    """One 32768-token sequence at head_dim 128 (64 q / 8 KV heads, sinks; q and out 512 MiB
+    each): up to 512 key tiles per work-group; positions 0-255, the last 64 and every 521st,
+    every query head, against the oracle's row routine."""
+    wl = workloads.custom([32768], 64, 8, window=window, head_dim=D, softmax_scale=SCALE, seed=0)
+    inp = workloads.make_inputs(wl)
+    say(f"d128 long sequence W={window} T={wl.total_tokens}")
+    got = f64(run_gpu(inp).cpu())
+    torch.cuda.synchronize()
+    L = wl.total_tokens
+    pos = np.unique(np.concatenate([np.arange(256), np.arange(L - 64, L), np.arange(0, L, 521)]))
+    rows = np.repeat(pos, wl.n_q_heads)
+    heads = np.tile(np.arange(wl.n_q_heads), pos.size)
+    ref = oracle.prefill_rows(*oracle_args(inp), rows=rows, heads=heads, lib=oracle_lib)
+    gate(got[rows, heads], ref.reshape(got[rows, heads].shape), f"d128 1x32768 W={window} sampled")
+
+
 @pytest.mark.parametrize("window", [0, 1, 127, 128, 129])
 def test_q_zero_closed_form_d128(window):
     """q = 0: every probability of a row is one number, so |err| <= 2^-7 |ref| (see the
