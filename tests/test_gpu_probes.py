@@ -241,6 +241,40 @@ def test_runs_on_a_side_stream(oracle_lib):
     assert_within_rounding(f64(got.cpu()), inp, oracle_lib)
 
 
+@pytest.mark.parametrize("head_dim,kernel,window", [(64, "wide", 0), (64, "narrow", 0),
+                                                     (64, "wide", 128), (128, "narrow", 100)])
+def test_graph_replay_matches_eager(head_dim, kernel, window, monkeypatch):
+    """A prefill call captured in a HIP graph gives the eager result bit for bit on every
+    replay, with other eager work and synchronisations between replays (the library records
+    no memset node and keeps no state between calls)."""
+    monkeypatch.setenv("TS_MHA_PREFILL_KERNEL", kernel)
+    wl = workloads.custom([700, 1, 2048, 65], 64, 8, window=window, head_dim=head_dim,
+                          softmax_scale=head_dim ** -0.5, seed=14)
+    inp = workloads.make_inputs(wl)
+    say(f"graph replay D={head_dim} {kernel} W={window}")
+    dev = torch.device("cuda", 0)
+    q, k, v = inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev)
+    sinks, cu = inp["sinks"].to(dev), inp["cu_seqlens"].to(dev)
+    kw = dict(window=window, softmax_scale=wl.softmax_scale, max_seqlen=wl.max_seqlen)
+    eager = tm.ts_mha_prefill(q, k, v, sinks, cu, **kw).clone()
+    out = torch.empty_like(q)
+    graph = torch.cuda.CUDAGraph()
+    gs = torch.cuda.Stream()
+    gs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(gs):
+        with torch.cuda.graph(graph, stream=gs):
+            tm.ts_mha_prefill(q, k, v, sinks, cu, out=out, **kw)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        other = tm.ts_mha_prefill(q, k, v, sinks, cu, **kw)  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+        assert torch.equal(other.view(torch.int16), eager.view(torch.int16)), f"eager {rep}"
+    del graph
+
+
 def test_arch_check_hook(monkeypatch):
     q = torch.zeros(4, 8, 64, dtype=torch.bfloat16, device="cuda")
     k = torch.zeros(4, 1, 64, dtype=torch.bfloat16, device="cuda")
