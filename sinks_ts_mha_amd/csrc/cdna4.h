@@ -21,6 +21,10 @@ typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBufferConfig = 0x00020000;  // raw buffer descriptor word 3 (32-bit data)
+// Cache policy of the output stores (nt | sc1): the rows are written once and
+// not read again by the kernel, so they stream out instead of taking L2 lines
+// that the K/V tiles other work-groups still read.
+constexpr int kStreamStore = 0x12;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Raw buffer descriptor (base, stride 0, byte range n) in scalar registers.

@@ -688,7 +688,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
       const int r = 64 * w + row;
       const int ch = el & 7;
       const u32x4 x = lds_q[w * 64 * kChunks + swz(row, ch)];
-      __builtin_amdgcn_raw_buffer_store_b128(x, ro, ((p0 + r / G) * Hq + g * G + r % G) * kRowBytes + ch * 16, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(x, ro, ((p0 + r / G) * Hq + g * G + r % G) * kRowBytes + ch * 16, 0, kStreamStore);
     }
   }
 }

@@ -548,7 +548,7 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 3 : 2) prefill_fwd_narrow(
       const int r = kQW * w + row;
       const int ch = el % kChunks;
       const u32x4 x = *(const u32x4*)(ob + tpos<D>(row, ch) * 16);
-      __builtin_amdgcn_raw_buffer_store_b128(x, ro, ((p0 + r / G) * Hq + g * G + r % G) * kRowBytes + ch * 16, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(x, ro, ((p0 + r / G) * Hq + g * G + r % G) * kRowBytes + ch * 16, 0, kStreamStore);
     }
   }
 }
