@@ -62,6 +62,22 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds, const i32x4& rsrc, int v
 #pragma clang diagnostic pop
 }
 
+// The same load with the non-temporal hint (nt), for data that one work-group
+// reads once per call (a decode step's cached keys and values): the lines
+// stream through the caches instead of displacing what others re-read.
+__device__ __forceinline__ void lds_dma16_nt(uint32_t lds, const i32x4& rsrc, int voffset) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen nt lds"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voffset), "s"(rsrc)
+      : "m0");
+#pragma clang diagnostic pop
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight.
 template <int N>
 __device__ __forceinline__ void wait_vmem() {

@@ -203,8 +203,8 @@ __global__ void __launch_bounds__(kThreads, 1) decode_split_d64(DParams p) {
         const int it = 2 * half + j;
         const int key = tile_key + 8 * it + (lane >> 3);
         const int vo = (live && key < end) ? (key & pmask) * Hkv * kRowBytes + dch[it] : p.page_bytes;
-        lds_dma16(dk + it * 1024, rk, vo);
-        lds_dma16(dk + kTileBytes + it * 1024, rv, vo);
+        lds_dma16_nt(dk + it * 1024, rk, vo);
+        lds_dma16_nt(dk + kTileBytes + it * 1024, rv, vo);
       }
     }
   };
