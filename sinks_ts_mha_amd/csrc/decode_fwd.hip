@@ -17,7 +17,8 @@
 // does not split a sequence when there are enough (sequence, KV head) pairs.  Its four waves take the chunk's
 // 32-key tiles round robin; each wave streams its tiles through a private
 // ring of four LDS stages with wave-wide buffer-to-LDS loads, three tiles
-// ahead, so the walk needs no barrier.
+// ahead, so the walk needs no barrier.  Every cached row is read once per
+// call, so the loads carry the non-temporal hint.
 //
 // Paging.  A 32-key tile is loaded as four groups of 8 keys; with pages of at
 // least 16 keys a group never straddles a page, so each load takes one page

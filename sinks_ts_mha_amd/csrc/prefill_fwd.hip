@@ -64,7 +64,8 @@
 // Output.  Each wave writes its normalised bf16 rows into its part of the
 // query staging area and reads them back whole, so every store instruction
 // writes complete 128-byte rows (1 KiB contiguous when the G heads of a
-// position are) rather than 16-byte pieces of 32 rows.
+// position are) rather than 16-byte pieces of 32 rows.  The stores carry a
+// streaming cache policy, so the output does not evict K/V lines from L2.
 #include "prefill_fwd.h"
 
 #include <math.h>
