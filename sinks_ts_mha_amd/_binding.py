@@ -13,7 +13,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libts_mha.so")
+# TS_MHA_LIBRARY names another build of the same library (the tests use it for a
+# build whose host code carries the address and undefined-behaviour sanitizers).
+LIB_PATH = os.environ.get("TS_MHA_LIBRARY") or os.path.join(_PKG, "libts_mha.so")
 
 TS_MHA_OK = 0
 ERROR_NAMES = {

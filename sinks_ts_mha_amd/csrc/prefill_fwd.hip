@@ -38,13 +38,14 @@
 // lands in the XOR-swizzled layout the readers expect.  The XOR pattern is laid
 // out for an LDS that serves 256 bytes (64 banks) per cycle.
 //
-// Softmax.  Base 2 throughout: t = s * scale * log2(e).  The query operand
-// is q * scale * log2(e) rounded once to bf16, so the score accumulators hold
-// t itself.  A row's result does not depend on the reference m its
-// probabilities exp2(t - m) are measured against, as long as nothing leaves
-// fp32 range; the fast pass takes m = 0 for every row, so a probability is
-// exp2 of its score accumulator: no running maximum, no rescaling, and the
-// per-element vector work is one exp2 and half a bf16 pack.  Row sums
+// Softmax.  Base 2 throughout: t = s * scale * log2(e), with s = q.k from
+// the MFMA (bf16 products exact, fp32 sums) and the product by scale * log2 e
+// taken in fp32, so no rounding beyond fp32's touches a logit.  A row's
+// result does not depend on the reference m its probabilities exp2(t - m) are
+// measured against, as long as nothing leaves fp32 range; the fast pass takes
+// m = 0 for every row, so a probability is exp2 of its scaled score: no
+// running maximum, no rescaling, and the per-element vector work is one
+// multiply, one exp2 and half a bf16 pack.  Row sums
 // accumulate on the matrix pipe (see row_sums).  If a row's sum leaves
 // [2^-64, 2^65) or a value stops being finite (logits beyond about +-64 in
 // base 2), the work-group redoes its rows with tile_exact, a streaming
@@ -184,7 +185,10 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   const int hi = lane >> 5;
   const int r16 = lane & 15;
   const int half16 = (lane >> 4) & 1;
-  const float c = p.c;
+  // scale * log2(e) in a VGPR, so that the per-score multiply takes the
+  // VGPR-only encoding (which two waves of a SIMD can issue in alternate cycles)
+  float cv = p.c;
+  asm volatile("" : "+v"(cv));
 
   const int last = qoff + min(L, p0 + P) - 1;
   const int first = WINDOWED ? max(0, qoff + p0 - p.window + 1) : 0;
@@ -304,17 +308,14 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   // still in flight.
   issue_tile(kt1, 0);
   wait_vmem<4>();  // the query rows have landed (loads complete in order; the tile's 4 may not)
-  // The query operand carries the softmax scale and log2 e, rounded once to
-  // bf16 (qf = q * c): the score accumulators then hold base-2 logits and the
-  // probabilities need no multiply.
+  // The query operand is the bf16 query itself, so every score accumulator
+  // holds q.k exactly up to fp32 summation; the scale (times log2 e) is
+  // applied to it in fp32 before the exponential.
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 x = __builtin_bit_cast(bf16x8, lds_q[w * 64 * kChunks + swz(32 * nb + l32, 2 * ks + hi)]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[nb][ks][e] = (__bf16)((float)x[e] * c);
-    }
+    for (int ks = 0; ks < 4; ++ks)
+      qf[nb][ks] = __builtin_bit_cast(bf16x8, lds_q[w * 64 * kChunks + swz(32 * nb + l32, 2 * ks + hi)]);
 
   // K fragments (A operand) of key half mb for the four 16-wide steps of head_dim.
   // Per-lane byte offsets of the operand reads within a tile, fixed for the
@@ -387,17 +388,17 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float pe = __builtin_amdgcn_exp2f(sc[e] - m);
+      const float pe = __builtin_amdgcn_exp2f(fmaf(sc[e], cv, -m));
       if (e < 8) plo[e] = (__bf16)pe; else phi[e - 8] = (__bf16)pe;
       if (e & 1) a1 += pe; else a0 += pe;
     }
     return a0 + a1;
   };
-  // Probabilities of the fast pass: against reference 1, exp2 of the score itself.
+  // Probabilities of the fast pass: against reference 1, exp2 of the scaled score.
   auto block_probs_fast = [&](const f32x16& sc, bf16x8& plo, bf16x8& phi) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float pe = __builtin_amdgcn_exp2f(sc[e]);
+      const float pe = __builtin_amdgcn_exp2f(sc[e] * cv);
       if (e < 8) plo[e] = (__bf16)pe; else phi[e - 8] = (__bf16)pe;
     }
   };
@@ -516,7 +517,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         const f32x16 sc = qk(mask_tag, ka, mb, nb, k0);
-        const float mx = pair_max(max16(sc));
+        // the largest scaled score (c > 0, and rounding is monotonic)
+        const float mx = pair_max(max16(sc)) * cv;
         if (mx > mref[nb]) {
           const float alpha = __builtin_amdgcn_exp2f(mref[nb] - mx);
           lsum[nb] *= alpha;
@@ -561,7 +563,6 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   using MBoth = std::integral_constant<int, kMaskCausal | (WINDOWED ? kMaskWindow : 0)>;
   using Lo = std::integral_constant<int, 0>;
   using Hi = std::integral_constant<int, 1>;
-  auto exact_masked = [&](const u32x4* kl, lds_char* vb, int k0) { tile_exact(MBoth{}, kl, vb, k0); };
   auto fast_both = [&](const u32x4* kl, lds_char* vb, int k0) { tile_fast(MBoth{}, kl, vb, k0); };
   auto fast_causal = [&](const u32x4* kl, lds_char* vb, int k0) { tile_fast(MCausal{}, kl, vb, k0); };
   auto fast_window = [&](const u32x4* kl, lds_char* vb, int k0) { tile_fast(MWindow{}, kl, vb, k0); };
@@ -624,7 +625,13 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
     lrow[nb] = (l32 < 16) ? e0 : e1;
   }
   // The fast pass is kept unless a row's sum left [2^-64, 2^65) or a sum or
-  // an output is not finite.  Then the work-group redoes its rows exactly.
+  // an output is not finite.  Then the rows are redone exactly.  The vote is
+  // taken per half of the work-group (waves 0-1 and 2-3: 128 rows each, the
+  // rows of one work-group of the 128-row kernel), so that a row's arithmetic
+  // does not depend on which of the two kernels ran it.  All four waves walk
+  // the redo, since each loads its part of every tile; a half whose fast
+  // result stands stores it first and only loads.
+  bool redo_mine = false, redo_any = false;
   {
     bool bad = false;
 #pragma unroll
@@ -640,14 +647,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
     const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
     if (lane == 0) redo_vote[w] = wave_bad ? 1 : 0;
     __syncthreads();
-    const bool redo = (redo_vote[0] | redo_vote[1] | redo_vote[2] | redo_vote[3]) != 0;
-    if (redo) {
-      reset();
-      issue_tile(kt1, 0);
-      walk(exact_masked, kt1, kt0);
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) lrow[nb] = pair_sum(lsum[nb]);
-    }
+    const int hv = 2 * (w >> 1);
+    redo_mine = (redo_vote[hv] | redo_vote[hv + 1]) != 0;
+    redo_any = (redo_vote[0] | redo_vote[1] | redo_vote[2] | redo_vote[3]) != 0;
   }
 
   // ---- epilogue: add the sink's term to the row sum, normalise, store.
@@ -658,29 +660,29 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   // G heads of a position are) instead of 16-byte pieces of 32 rows.  Rows
   // past the sequence end fall outside the output descriptor's range and are
   // dropped.
-  // The lane index is laundered so that no address term of the query loads,
-  // which share these offsets, is kept live through the walk to be reused.
-  int el = lane;
-  asm volatile("" : "+v"(el));
-  const int el32 = el & 31, ehi = el >> 5;
-  u32x2* const lds_o = reinterpret_cast<u32x2*>(&lds_q[w * 64 * kChunks]);
+  auto store_rows = [&]() {
+    // The lane index is laundered so that no address term of the query loads,
+    // which share these offsets, is kept live through the walk to be reused.
+    int el = lane;
+    asm volatile("" : "+v"(el));
+    const int el32 = el & 31, ehi = el >> 5;
+    u32x2* const lds_o = reinterpret_cast<u32x2*>(&lds_q[w * 64 * kChunks]);
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    float lt = lrow[nb];
-    if (p.sinks) lt += __builtin_amdgcn_exp2f(sink_t(nb) - mref[nb]);
-    const float inv = 1.f / lt;
+    for (int nb = 0; nb < 2; ++nb) {
+      float lt = lrow[nb];
+      if (p.sinks) lt += __builtin_amdgcn_exp2f(sink_t(nb) - mref[nb]);
+      const float inv = 1.f / lt;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+      for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int vg = 0; vg < 4; ++vg) {
-        // head_dim elements 32 db + 8 vg + 4 hi .. + 3: half hi of chunk 4 db + vg
-        bf16x4 val;
+        for (int vg = 0; vg < 4; ++vg) {
+          // head_dim elements 32 db + 8 vg + 4 hi .. + 3: half hi of chunk 4 db + vg
+          bf16x4 val;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) val[e] = (__bf16)(o[db][nb][4 * vg + e] * inv);
-        lds_o[2 * swz(32 * nb + el32, 4 * db + vg) + ehi] = __builtin_bit_cast(u32x2, val);
-      }
-  }
-  {
+          for (int e = 0; e < 4; ++e) val[e] = (__bf16)(o[db][nb][4 * vg + e] * inv);
+          lds_o[2 * swz(32 * nb + el32, 4 * db + vg) + ehi] = __builtin_bit_cast(u32x2, val);
+        }
+    }
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(p.out + (int64_t)s * Hq * kD), 0, L * Hq * kRowBytes, kBufferConfig);
 #pragma unroll
@@ -691,7 +693,22 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
       const u32x4 x = lds_q[w * 64 * kChunks + swz(row, ch)];
       __builtin_amdgcn_raw_buffer_store_b128(x, ro, ((p0 + r / G) * Hq + g * G + r % G) * kRowBytes + ch * 16, 0, kStreamStore);
     }
+  };
+
+  if (redo_any) {
+    if (redo_mine) reset();
+    else store_rows();
+    auto redo_tile = [&](const u32x4* kl, lds_char* vb, int k0) {
+      if (redo_mine) tile_exact(MBoth{}, kl, vb, k0);
+    };
+    issue_tile(kt1, 0);
+    walk(redo_tile, kt1, kt0);
+    if (redo_mine) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) lrow[nb] = pair_sum(lsum[nb]);
+    }
   }
+  if (!redo_any || redo_mine) store_rows();
 }
 
 namespace {

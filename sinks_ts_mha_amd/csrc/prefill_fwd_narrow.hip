@@ -36,8 +36,8 @@
 // transposed V reads) each hit distinct banks of the 64-bank LDS; 128-byte
 // rows use the swizzle of cdna4.h, laid out for the same access patterns.
 //
-// Softmax.  As in prefill_fwd.hip: base 2, scale * log2(e) folded into the bf16
-// query operand, every probability exp2 of its score against reference 1,
+// Softmax.  As in prefill_fwd.hip: base 2, scale * log2(e) applied to each fp32
+// score, every probability exp2 of its scaled score against reference 1,
 // row sums on the matrix pipe, and a streaming softmax with running maxima for
 // a work-group whose sums leave [2^-64, 2^65).
 #include <math.h>
@@ -155,7 +155,10 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 3 : 2) prefill_fwd_narrow(
   const int hi = lane >> 5;
   const int r16 = lane & 15;
   const int half16 = (lane >> 4) & 1;
-  const float c = p.c;
+  // scale * log2(e) in a VGPR, so that the per-score multiply takes the
+  // VGPR-only encoding
+  float cv = p.c;
+  asm volatile("" : "+v"(cv));
 
   const int last = min(L, p0 + P) - 1;
   const int first = WINDOWED ? max(0, p0 - p.window + 1) : 0;
@@ -217,18 +220,14 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 3 : 2) prefill_fwd_narrow(
   }
   issue_tile(kt1, 0);
   wait_vmem<2 * S::kTileLoads>();  // the query rows have landed (the tile's loads may not)
-  // Query operand (B of the score MFMA) for the eight 16-wide steps of
-  // head_dim: lane l holds elements 16 ks + 8 hi .. + 7 of its row, times
-  // scale * log2(e), rounded once to bf16.
+  // Query operand (B of the score MFMA) for the D / 16 steps of head_dim:
+  // lane l holds elements 16 ks + 8 hi .. + 7 of its row, the bf16 query
+  // itself (the scale is applied to the fp32 scores).
   bf16x8 qf[KS];
   {
     const lds_char* qb = (w < 2 ? (const lds_char*)lds_k : (const lds_char*)lds_v) + kTileBytes + (w & 1) * kQW * kRowBytes;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 x = *(const bf16x8*)(qb + tpos<D>(l32, 2 * ks + hi) * 16);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)((float)x[e] * c);
-    }
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const bf16x8*)(qb + tpos<D>(l32, 2 * ks + hi) * 16);
   }
 
   // Per-lane byte offsets of the operand reads within a tile, fixed for the
@@ -285,11 +284,13 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 3 : 2) prefill_fwd_narrow(
     return acc;
   };
   // bf16 P^T of one score block in the PV B-operand order (plo: PV step 2 mb,
-  // phi: step 2 mb + 1), against reference m (the fast pass: m = 0).
-  auto probs = [&](const f32x16& sc, float m, bf16x8& plo, bf16x8& phi) {
+  // phi: step 2 mb + 1): the fast pass's exp2(scale * log2 e * s) against
+  // reference 1, and the exact pass's against reference m with the lane's
+  // sum of the fp32 values.
+  auto probs = [&](const f32x16& sc, bf16x8& plo, bf16x8& phi) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float pe = __builtin_amdgcn_exp2f(sc[e] - m);
+      const float pe = __builtin_amdgcn_exp2f(sc[e] * cv);
       if (e < 8) plo[e] = (__bf16)pe; else phi[e - 8] = (__bf16)pe;
     }
   };
@@ -297,7 +298,7 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 3 : 2) prefill_fwd_narrow(
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float pe = __builtin_amdgcn_exp2f(sc[e] - m);
+      const float pe = __builtin_amdgcn_exp2f(fmaf(sc[e], cv, -m));
       if (e < 8) plo[e] = (__bf16)pe; else phi[e - 8] = (__bf16)pe;
       if (e & 1) a1 += pe; else a0 += pe;
     }
@@ -351,7 +352,7 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 3 : 2) prefill_fwd_narrow(
     __builtin_amdgcn_sched_barrier(0);
     read_k(kl, 1, ka);
     const f32x16 s1 = qk(mask_tag, ka, 1, k0);
-    probs(s0, 0.f, pf[0], pf[1]);
+    probs(s0, pf[0], pf[1]);
 #pragma unroll
     for (int db = 0; db < DB; ++db) va[db] = read_v(vb, 0, db);
     interleave(std::integral_constant<int, KS>{}, std::integral_constant<int, 24 / KS>{});
@@ -364,7 +365,7 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 3 : 2) prefill_fwd_narrow(
 #pragma unroll
     for (int db = 0; db < DB; ++db) vn[db] = read_v(vb, 1, db);
     pv_step(va, pf[0]);
-    probs(s1, 0.f, pf[2], pf[3]);
+    probs(s1, pf[2], pf[3]);
 #pragma unroll
     for (int db = 0; db < DB; ++db) va[db] = read_v(vb, 2, db);
     pv_step(vn, pf[1]);
@@ -385,7 +386,7 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 3 : 2) prefill_fwd_narrow(
     const f32x16 sc = qk(mask_tag, ka, mb, k0);
     __builtin_amdgcn_sched_barrier(0);
     read_v2(vb, 2 * mb, va);
-    probs(sc, 0.f, pf[2 * mb], pf[2 * mb + 1]);
+    probs(sc, pf[2 * mb], pf[2 * mb + 1]);
     __builtin_amdgcn_sched_barrier(0);
     pv2(va, pf, 2 * mb);
 #pragma unroll
@@ -399,7 +400,8 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 3 : 2) prefill_fwd_narrow(
       bf16x8 ka[KS], pf[4];
       read_k(kl, mb, ka);
       const f32x16 sc = qk(std::integral_constant<int, kMaskCausal | (WINDOWED ? kMaskWindow : 0)>{}, ka, mb, k0);
-      const float mx = pair_max(max16(sc));
+      // the largest scaled score (c > 0, and rounding is monotonic)
+      const float mx = pair_max(max16(sc)) * cv;
       if (mx > mref) {
         const float alpha = __builtin_amdgcn_exp2f(mref - mx);
         lsum *= alpha;

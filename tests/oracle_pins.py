@@ -302,7 +302,29 @@ def pin_scale_homogeneity(lib):
     assert not np.allclose(a, c), "the scale must change the result"
 
 
-ALL_PINS = [pin_sdpa_no_sink, pin_sdpa_sink_augmented, pin_closed_form_q_zero,
+def pin_rows_equal_prefill(lib):
+    """The selected-rows routine gives, bit for bit, the rows of the full routine (which
+    the pins above tie to the library routine and the closed forms): ragged packs with
+    empty sequences, windows 0, 1, 5 and one covering every sequence, sinks on and off,
+    rows in shuffled order with repeats, both head widths."""
+    seqlens = [0, 7, 1, 0, 33, 64, 65, 0, 130]
+    cases = [(w, sk, 64) for w in (0, 1, 5, 200) for sk in (True, False)] + [(5, True, 128), (0, False, 128)]
+    for n, (window, sinks, head_dim) in enumerate(cases):
+        inp = _inputs(seqlens, 8, 2, window=window, sinks=sinks, seed=300 + n, head_dim=head_dim,
+                      scale=head_dim ** -0.5)
+        full = _run(lib, inp)
+        T, hq = full.shape[0], full.shape[1]
+        g = torch.Generator().manual_seed(400 + n)
+        pick = torch.randperm(T * hq, generator=g)
+        pick = torch.cat([pick, pick[:17]])          # repeats
+        rows = (pick // hq).numpy().astype(np.int64)
+        heads = (pick % hq).numpy().astype(np.int32)
+        got = oracle.prefill_rows(*oracle_args(inp), rows=rows, heads=heads, lib=lib)
+        assert np.array_equal(got, full[rows, heads]), \
+            f"rows routine differs from the full routine (W={window} sinks={sinks} D={head_dim})"
+
+
+ALL_PINS = [pin_rows_equal_prefill, pin_sdpa_no_sink, pin_sdpa_sink_augmented, pin_closed_form_q_zero,
             pin_closed_form_window_one, pin_hand_example, pin_sink_extremes,
             pin_probs_sum_to_one, pin_window_covering_equals_full, pin_packed_equals_separate,
             pin_permute_sequences, pin_causality, pin_head_groups, pin_scale_homogeneity]

@@ -1,10 +1,11 @@
 """HIP path vs the fp64 oracle, element by element, through the C ABI.
 
 Gate (every case): max |gpu - oracle| <= 2e-2 and mean |gpu - oracle| <= 2e-3 on
-the bf16 outputs.  Small cases also pass a tighter elementwise bound derived
-from the kernel's roundings (bf16 probabilities, bf16 output; see
-_util.rounding_bound) against the oracle on the kernel's bf16 query operand in
-base 2 (_util.base2_inputs), which a wrong mask, sink or head mapping would break.
+the bf16 outputs.  Small cases and the sampled rows of the long workloads also
+pass a tighter elementwise bound derived from the kernel's roundings (bf16
+probabilities, bf16 output, fp32 accumulation over the row's keys; see
+_util.rounding_bound), which a wrong mask, sink or head mapping would break
+where the gate cannot see it.
 """
 import numpy as np
 import pytest
@@ -12,7 +13,7 @@ import torch
 
 from oracle import oracle
 from sinks_ts_mha_amd import workloads
-from _util import assert_within_rounding, err_stats, f64, oracle_args, run_gpu, say
+from _util import assert_within_rounding, err_stats, f64, oracle_args, rounding_bound, run_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -94,6 +95,13 @@ def test_long_prefill_sampled_rows(oracle_lib):
     heads = np.tile(np.arange(wl.n_q_heads), pos.size)
     ref = oracle.prefill_rows(*oracle_args(inp), rows=rows, heads=heads, lib=oracle_lib)
     check(got[rows, heads], ref, "long_1x32768 sampled")
+    # The gate cannot see a dropped sink or a key too many on rows this long; the
+    # elementwise bound (bf16 roundings, fp32 accumulation over up to 32768 keys) can.
+    bound = rounding_bound(inp, ref, oracle_lib, rows=rows, heads=heads)
+    excess = np.abs(got[rows, heads] - ref) - bound
+    print(f"  long_1x32768 rounding bound: max excess {excess.max():.3e}, "
+          f"max err/bound {(np.abs(got[rows, heads] - ref) / bound).max():.3f}", flush=True)
+    assert excess.max() <= 0, f"rounding bound exceeded by {excess.max():.3e}"
 
 
 # 1x1K, 2x1K and 1x2K run the 128-row kernel (their 256-row grids would leave CU slots empty)
@@ -122,3 +130,5 @@ def test_chart_point_sampled_rows(name, oracle_lib):
     heads = np.tile(np.arange(wl.n_q_heads), pos.size)
     ref = oracle.prefill_rows(*oracle_args(inp), rows=rows, heads=heads, lib=oracle_lib)
     check(got[rows, heads], ref, f"{name} sampled")
+    excess = np.abs(got[rows, heads] - ref) - rounding_bound(inp, ref, oracle_lib, rows=rows, heads=heads)
+    assert excess.max() <= 0, f"{name}: rounding bound exceeded by {excess.max():.3e}"

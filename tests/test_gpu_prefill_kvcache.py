@@ -1,8 +1,7 @@
 """Prefill of new rows against a paged KV cache: HIP path vs the fp64 oracle's cache form.
 
 Gate (every case): max |gpu - oracle| <= 2e-2 and mean |gpu - oracle| <= 2e-3, plus the
-elementwise rounding bound on the small cases, against the oracle on the attention the
-kernel evaluates (_util.base2_inputs: the query operand carries the scale).  The cases cover chunks that are the whole
+elementwise rounding bound on the small cases, against the same oracle rows.  The cases cover chunks that are the whole
 sequence, chunks at the end of a longer cache, single rows, every group size, page sizes
 16..256, windows around tile edges and empty sequences; with the whole sequence as the chunk
 the result must equal ts_mha_prefill on the same data bit for bit.
@@ -14,8 +13,8 @@ import torch
 import sinks_ts_mha_amd as tm
 from oracle import oracle
 from sinks_ts_mha_amd import workloads
-from _util import (base2_inputs, cache_oracle_args, cache_rounding_bound, err_stats, f64,
-                   run_gpu, run_gpu_prefill_kv, say)
+from _util import (cache_oracle_args, cache_rounding_bound, err_stats, f64, run_gpu,
+                   run_gpu_prefill_kv, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -66,12 +65,8 @@ def test_prefill_kvcache_small_parity(case, oracle_lib):
     got = f64(run_gpu_prefill_kv(inp).cpu())
     torch.cuda.synchronize()
     ref = oracle.cache_attend(*cache_oracle_args(inp), lib=oracle_lib)
-    check(got, ref, f"q_lens={q_lens} G={hq // hkv} page={page} W={w}")
-    # the elementwise bound, against the attention the kernel evaluates
-    b2 = base2_inputs(inp)
-    ref2 = oracle.cache_attend(*cache_oracle_args(b2), lib=oracle_lib)
-    check(got, ref2, "  base-2 form of the kernel's query operand",
-          bound=cache_rounding_bound(b2, ref2, oracle_lib))
+    check(got, ref, f"q_lens={q_lens} G={hq // hkv} page={page} W={w}",
+          bound=cache_rounding_bound(inp, ref, oracle_lib))
 
 
 def _paged_copy(inp, page_size, seed):

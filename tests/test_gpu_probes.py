@@ -115,11 +115,12 @@ def test_sink_values(sink, oracle_lib):
 @pytest.mark.parametrize("with_sinks", [True, False], ids=["sinks", "nosinks"])
 def test_wide_logit_range(window, with_sinks, seed, kernel, oracle_lib, monkeypatch):
     """Queries scaled by 40 spread each row's logits over hundreds of log2 units,
-    so measured against the row's own key many probabilities overflow fp32 (or
-    their sums pass 2^64) in the fast pass.  Those work-groups must redo their
-    rows with running maxima; every row still meets the rounding bound.  With seed
-    19 some work-groups' row sums come out NaN (an infinite probability times a
-    zero of the row-sum selector): the range test must catch NaN too."""
+    so measured against reference 1 many probabilities overflow fp32 (or their
+    sums pass 2^64) in the fast pass.  Those work-groups must redo their rows
+    with running maxima; every row still meets the rounding bound and the gate
+    against the oracle on the same inputs.  With seed 19 some work-groups' row
+    sums come out NaN (an infinite probability times a zero of the row-sum
+    selector): the range test must catch NaN too."""
     monkeypatch.setenv("TS_MHA_PREFILL_KERNEL", kernel)
     wl = workloads.custom([700, 333, 64, 5], 16, 2, window=window, seed=seed)
     inp = workloads.make_inputs(wl)
@@ -129,10 +130,26 @@ def test_wide_logit_range(window, with_sinks, seed, kernel, oracle_lib, monkeypa
     say(f"wide logit range window={window} sinks={with_sinks} seed={seed}")
     got = f64(run_gpu(inp).cpu())
     assert np.all(np.isfinite(got))
-    # Logits this spread make the query operand's rounding (relative 2^-8) move
-    # near-tied probabilities far more than the gate allows, so only the
-    # elementwise bound against the attention the kernel evaluates applies.
-    assert_within_rounding(got, inp, oracle_lib, gate=False)
+    assert_within_rounding(got, inp, oracle_lib, what=f"W={window} sinks={with_sinks} seed={seed}")
+
+
+@pytest.mark.parametrize("head_dim,kernel", [(64, "wide"), (64, "narrow"), (128, "narrow")])
+@pytest.mark.parametrize("spread", [2.0, 4.0, 8.0, 16.0])
+def test_logit_spread_gate(spread, head_dim, kernel, oracle_lib, monkeypatch):
+    """Queries scaled by 2 .. 16 make attention ever more peaked (logit standard deviation
+    2 .. 16 at scale 1/sqrt(head_dim)), the range where trained attention lives.  The
+    kernels take q.k exactly (bf16 products, fp32 sums) and apply the scale in fp32, so no
+    rounding of the logits grows with their spread: the rounding bound and the gate hold
+    against the oracle on the original inputs at every spread."""
+    monkeypatch.setenv("TS_MHA_PREFILL_KERNEL", kernel)
+    wl = workloads.custom([700, 333, 64, 5], 16, 2, window=0, head_dim=head_dim,
+                          softmax_scale=head_dim ** -0.5, seed=23)
+    inp = workloads.make_inputs(wl)
+    inp["q"] = (inp["q"].to(torch.float32) * spread).to(torch.bfloat16)
+    say(f"logit spread x{spread} D={head_dim} {kernel}")
+    got = f64(run_gpu(inp).cpu())
+    assert np.all(np.isfinite(got))
+    assert_within_rounding(got, inp, oracle_lib, what=f"spread x{spread} D={head_dim} {kernel}")
 
 
 def test_edge_shapes(oracle_lib):
@@ -177,18 +194,23 @@ def test_packed_equals_alone_bitwise():
         assert torch.equal(alone.view(torch.int16), packed[s:e].view(torch.int16)), f"sequence {b}"
 
 
+@pytest.mark.parametrize("qscale", [1.0, 40.0], ids=["fast", "redo"])
 @pytest.mark.parametrize("shape", [([70, 1, 300, 129, 0, 64], 16, 2, 100), ([1000, 333], 64, 8, 0),
                                    ([2048] * 2, 64, 8, 128), ([517, 65, 1], 32, 2, 0), ([300], 8, 8, 0)],
                          ids=["ragged_w100", "g8", "g8_w128", "g16", "g1"])
-def test_wide_and_narrow_kernels_agree_bitwise(shape, monkeypatch):
+def test_wide_and_narrow_kernels_agree_bitwise(shape, qscale, monkeypatch):
     """At head_dim 64 the launch picks the 256- or the 128-row work-groups by grid
     size; for each row both walk its visible keys with the same instructions in the
     same order (the extra keys either kind covers are masked or skipped and add exact
-    zeros), so their outputs are identical bit for bit."""
+    zeros), so their outputs are identical bit for bit.  Queries scaled by 40 make some
+    work-groups redo their rows exactly; the 256-row kernel decides that per half of
+    its rows, which are the rows of one 128-row work-group, so the redo does not break
+    the equality either."""
     seqlens, hq, hkv, w = shape
     wl = workloads.custom(seqlens, hq, hkv, window=w, seed=12)
     inp = workloads.make_inputs(wl)
-    say(f"wide vs narrow {shape}")
+    inp["q"] = (inp["q"].to(torch.float32) * qscale).to(torch.bfloat16)
+    say(f"wide vs narrow {shape} q x{qscale}")
     monkeypatch.setenv("TS_MHA_PREFILL_KERNEL", "wide")
     a = run_gpu(inp).cpu()
     monkeypatch.setenv("TS_MHA_PREFILL_KERNEL", "narrow")

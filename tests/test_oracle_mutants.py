@@ -46,6 +46,18 @@ MUTANTS = [
     ("sink_share_unshifted", "*p_sink = (sigma == -INFINITY) ? 0.0 : exp(sigma - m) / den;",
      "*p_sink = (sigma == -INFINITY) ? 0.0 : exp(sigma) / den;"),
     ("bf16_widening_wrong_half", "uint32_t w = ((uint32_t)bits) << 16;", "uint32_t w = ((uint32_t)bits) << 15;"),
+    # the selected-rows routine
+    ("rows_start_of_previous_sequence",
+     "seq_of_row(cu_seqlens, n_seqs, rows[n]);\n        const int64_t s = cu_seqlens[b];",
+     "seq_of_row(cu_seqlens, n_seqs, rows[n]);\n        const int64_t s = cu_seqlens[b > 0 ? b - 1 : 0];",
+     # keeps the mutant memory-safe: a row may now see more keys than its sequence holds
+     "double* z = (double*)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));",
+     "double* z = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));"),
+    ("rows_output_in_reverse_order", "out + n * (int64_t)head_dim, NULL, NULL",
+     "out + (n_rows - 1 - n) * (int64_t)head_dim, NULL, NULL"),
+    ("rows_head_of_first_entry", "rows[n] - s, heads[n], n_q_heads", "rows[n] - s, heads[0], n_q_heads"),
+    ("rows_query_one_position_early", "rows[n] - s, heads[n], n_q_heads",
+     "rows[n] - s - (rows[n] > s), heads[n], n_q_heads"),
     # the paged-cache form
     ("cache_top_left_alignment",
      "const int64_t p = (int64_t)seqlens_k[b] - q_len + (t - cu_seqlens_q[b]);",
