@@ -31,8 +31,10 @@
  * General rules for every entry point:
  *  - Every pointer named "device" must point to device memory of the current
  *    HIP device; the caller owns all buffers (a decode workspace included) and
- *    keeps them alive until the work on `stream` has finished.  The library
- *    allocates no device memory and keeps no per-call state.
+ *    keeps them alive until the work on `stream` has finished.  No call
+ *    allocates device memory or keeps per-call state; the one piece of device
+ *    memory the library owns is the fixed scratch array of
+ *    ts_mha_decode_with_kvcache_noalloc (below), one per GPU.
  *  - Arguments are validated on the host before any HIP call; a rejected call
  *    launches nothing and returns a negative TS_MHA_ERR_* code.  No C++
  *    exception crosses this interface.
@@ -69,7 +71,8 @@ extern "C" {
                                         cu_seqlens decreasing, or a length above max_seqlen; for the
                                         cache calls a seqlens_k entry outside [0, max_seqlen_k] or
                                         below the sequence's new-row count */
-#define TS_MHA_ERR_WORKSPACE (-10)   /* decode: workspace NULL or smaller than ts_mha_decode_workspace_size */
+#define TS_MHA_ERR_WORKSPACE (-10)   /* decode: workspace NULL or smaller than ts_mha_decode_workspace_size;
+                                        noalloc decode: more than TS_MHA_NOALLOC_SCRATCH_BYTES needed */
 #define TS_MHA_ERR_PAGES (-11)       /* only with TS_MHA_VALIDATE=1: a block-table entry that a sequence
                                         needs is outside [0, n_pages) */
 
@@ -234,6 +237,38 @@ int ts_mha_decode_with_kvcache(const void* q, const void* k_cache, const void* v
  */
 int64_t ts_mha_decode_workspace_size(int32_t n_seqs, int32_t n_q_heads, int32_t n_kv_heads,
                                      int32_t head_dim, int32_t window, int32_t max_seqlen_k);
+
+/*
+ * ts_mha_decode_with_kvcache_noalloc -- ts_mha_decode_with_kvcache for callers
+ * that cannot allocate device memory (work captured into a HIP graph, serving
+ * loops that may not call hipMalloc, harnesses that forbid it): the same
+ * operation, kernels and results, with the partial results of split
+ * sequences kept in a scratch array of the library instead of a caller's
+ * workspace.  The call allocates nothing: no hipMalloc, no hipFree, no
+ * allocating library routine.
+ *
+ *  Arguments as for ts_mha_decode_with_kvcache without workspace and
+ *  workspace_bytes.
+ *  Scratch: TS_MHA_NOALLOC_SCRATCH_BYTES (16 MiB) of device memory per GPU the
+ *  library runs on, held from the first call on that GPU until the process
+ *  ends, and shared by every call on that GPU.  A call whose split needs more
+ *  (ts_mha_decode_workspace_size above that figure) returns
+ *  TS_MHA_ERR_WORKSPACE and launches nothing.  Calls that overlap on one GPU
+ *  (on different streams, or from different threads without ordering) race on
+ *  the scratch and give undefined results; calls on one stream are ordered.
+ *  The scratch needs no initialisation; its contents after a call are
+ *  meaningless.  TS_MHA_VALIDATE is ignored here (its check reads the
+ *  arguments back, which allocates host memory and synchronises).
+ *  Returns TS_MHA_OK or a TS_MHA_ERR_* code.
+ */
+#define TS_MHA_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+int ts_mha_decode_with_kvcache_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                       const float* sinks, const int32_t* seqlens_k,
+                                       const int32_t* block_table, int32_t n_q_heads,
+                                       int32_t n_kv_heads, int32_t head_dim, int32_t window,
+                                       float softmax_scale, void* out, int32_t n_seqs,
+                                       int32_t n_pages, int32_t page_size, int32_t pages_per_seq,
+                                       int32_t max_seqlen_k, void* stream);
 
 #ifdef __cplusplus
 }

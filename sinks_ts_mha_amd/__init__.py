@@ -7,10 +7,12 @@ synthetic workload generators.
 """
 from ._binding import (TsMhaError, lib, mha_decode_with_kvcache, mha_prefill,
                        mha_prefill_with_kvcache, ts_mha_decode_with_kvcache,
-                       ts_mha_decode_workspace_size, ts_mha_prefill, ts_mha_prefill_with_kvcache,
-                       ts_mha_strerror, ts_mha_unmasked_pairs)
+                       ts_mha_decode_with_kvcache_noalloc, ts_mha_decode_workspace_size,
+                       ts_mha_prefill, ts_mha_prefill_with_kvcache, ts_mha_strerror,
+                       ts_mha_unmasked_pairs)
 
 __all__ = ["TsMhaError", "lib", "mha_decode_with_kvcache", "mha_prefill",
-           "mha_prefill_with_kvcache", "ts_mha_decode_with_kvcache", "ts_mha_decode_workspace_size",
+           "mha_prefill_with_kvcache", "ts_mha_decode_with_kvcache",
+           "ts_mha_decode_with_kvcache_noalloc", "ts_mha_decode_workspace_size",
            "ts_mha_prefill", "ts_mha_prefill_with_kvcache", "ts_mha_strerror",
            "ts_mha_unmasked_pairs"]

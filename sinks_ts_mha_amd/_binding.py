@@ -58,6 +58,10 @@ def lib() -> ctypes.CDLL:
                                                   ctypes.c_float, vp, i32, i32, i32, i32, i32, i32,
                                                   vp]
         L.ts_mha_prefill_with_kvcache.restype = ctypes.c_int
+        L.ts_mha_decode_with_kvcache_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                                         ctypes.c_float, vp, i32, i32, i32, i32, i32,
+                                                         vp]
+        L.ts_mha_decode_with_kvcache_noalloc.restype = ctypes.c_int
         L.ts_mha_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
         L.ts_mha_decode_workspace_size.restype = i64
         _lib = L
@@ -285,6 +289,39 @@ def ts_mha_decode_with_kvcache(q: torch.Tensor, k_cache: torch.Tensor, v_cache: 
         None if sinks is None else sinks.data_ptr(), seqlens_k.data_ptr(), block_table.data_ptr(),
         hq, hkv, D, int(window), float(softmax_scale), out.data_ptr(), B, n_pages, page_size,
         block_table.shape[1], int(max_seqlen_k), ws_ptr, ws_bytes, _stream_handle(stream, dev))
+    if rc != TS_MHA_OK:
+        raise TsMhaError(rc, ts_mha_strerror(rc))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024  # TS_MHA_NOALLOC_SCRATCH_BYTES
+
+
+def ts_mha_decode_with_kvcache_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                       sinks, seqlens_k: torch.Tensor, block_table: torch.Tensor,
+                                       window: int = 0, softmax_scale: float | None = None, out=None,
+                                       max_seqlen_k: int | None = None, stream=None) -> torch.Tensor:
+    """ts_mha_decode_with_kvcache with the split partials in the library's own scratch
+    (no workspace, no device allocation by the call; pass `out` to allocate nothing here
+    either).  Calls that overlap on one GPU race on that scratch."""
+    dev = q.device
+    B, hq, D = q.shape
+    _check_cache(q, k_cache, v_cache, sinks, seqlens_k, block_table, B)
+    n_pages, page_size, hkv, _ = k_cache.shape
+    out = _check_out(out, q, (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                              ("seqlens_k", seqlens_k), ("block_table", block_table),
+                              ("sinks", sinks)))
+    if softmax_scale is None:
+        softmax_scale = 1.0 / (D ** 0.5)
+    if B == 0:
+        return out
+    if max_seqlen_k is None:
+        max_seqlen_k = int(seqlens_k.max().cpu())
+    rc = lib().ts_mha_decode_with_kvcache_noalloc(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        None if sinks is None else sinks.data_ptr(), seqlens_k.data_ptr(), block_table.data_ptr(),
+        hq, hkv, D, int(window), float(softmax_scale), out.data_ptr(), B, n_pages, page_size,
+        block_table.shape[1], int(max_seqlen_k), _stream_handle(stream, dev))
     if rc != TS_MHA_OK:
         raise TsMhaError(rc, ts_mha_strerror(rc))
     return out

@@ -30,6 +30,16 @@ std::mutex g_arch_mutex;
 
 thread_local char g_launch_msg[256] = "";
 
+// Scratch of ts_mha_decode_with_kvcache_noalloc: the per-chunk partial results
+// of split sequences, in a device array of the library itself instead of a
+// caller's workspace.  Each device the library runs on holds its own copy
+// until the process ends.  In host code `scratch` is only a stand-in for the
+// symbol: its device address, per device, comes from hipGetSymbolAddress on
+// the first call on that device and is kept in g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[TS_MHA_NOALLOC_SCRATCH_BYTES];
+void* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 int check_device(int* cus = nullptr) {
@@ -288,14 +298,38 @@ extern "C" int64_t ts_mha_decode_workspace_size(int32_t n_seqs, int32_t n_q_head
   return plan.workspace_bytes;
 }
 
-extern "C" int ts_mha_decode_with_kvcache(const void* q, const void* k_cache, const void* v_cache,
-                                          const float* sinks, const int32_t* seqlens_k,
-                                          const int32_t* block_table, int32_t n_q_heads,
-                                          int32_t n_kv_heads, int32_t head_dim, int32_t window,
-                                          float softmax_scale, void* out, int32_t n_seqs,
-                                          int32_t n_pages, int32_t page_size, int32_t pages_per_seq,
-                                          int32_t max_seqlen_k, void* workspace,
-                                          int64_t workspace_bytes, void* stream) {
+namespace {
+
+// This device's copy of `scratch`, looked up on the device's first call.
+int scratch_for_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return TS_MHA_ERR_NO_DEVICE;
+  }
+  if (dev >= kMaxDevices) return TS_MHA_ERR_ARCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || !p) {
+      snprintf(g_launch_msg, sizeof g_launch_msg, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(err));
+      (void)hipGetLastError();
+      return TS_MHA_ERR_LAUNCH;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return TS_MHA_OK;
+}
+
+// Both decode entry points: the caller's workspace, or (noalloc) the library's scratch.
+int decode_call(const void* q, const void* k_cache, const void* v_cache, const float* sinks,
+                const int32_t* seqlens_k, const int32_t* block_table, int32_t n_q_heads,
+                int32_t n_kv_heads, int32_t head_dim, int32_t window, float softmax_scale, void* out,
+                int32_t n_seqs, int32_t n_pages, int32_t page_size, int32_t pages_per_seq,
+                int32_t max_seqlen_k, void* workspace, int64_t workspace_bytes, bool noalloc,
+                void* stream) {
   if (!q || !k_cache || !v_cache || !seqlens_k || !block_table || !out) return TS_MHA_ERR_NULL_ARG;
   int rc = check_cache_shapes(n_q_heads, n_kv_heads, head_dim, softmax_scale, n_seqs, n_pages, page_size,
                               pages_per_seq, max_seqlen_k);
@@ -317,16 +351,24 @@ extern "C" int ts_mha_decode_with_kvcache(const void* q, const void* k_cache, co
   a.pages_per_seq = pages_per_seq;
   const tsmha::DecodePlan plan = tsmha::decode_plan(a);
   if (plan.n_splits < 0) return TS_MHA_ERR_BAD_SHAPE;
-  if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+  if (noalloc) {
+    if (plan.workspace_bytes > TS_MHA_NOALLOC_SCRATCH_BYTES) return TS_MHA_ERR_WORKSPACE;
+  } else if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes)) {
     return TS_MHA_ERR_WORKSPACE;
+  }
 
   rc = check_device();
   if (rc != TS_MHA_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const char* dbg = getenv("TS_MHA_VALIDATE");
-  if (dbg && dbg[0] == '1' && n_seqs > 0) {
-    rc = validate_cache(seqlens_k, block_table, n_seqs, n_pages, page_size, pages_per_seq, max_seqlen_k, st);
+  if (noalloc) {
+    rc = scratch_for_current_device(&workspace);
     if (rc != TS_MHA_OK) return rc;
+  } else {
+    const char* dbg = getenv("TS_MHA_VALIDATE");
+    if (dbg && dbg[0] == '1' && n_seqs > 0) {
+      rc = validate_cache(seqlens_k, block_table, n_seqs, n_pages, page_size, pages_per_seq, max_seqlen_k, st);
+      if (rc != TS_MHA_OK) return rc;
+    }
   }
   if (n_seqs == 0) return TS_MHA_OK;
   const hipError_t err = tsmha::launch_decode(a, plan, workspace, st);
@@ -335,6 +377,34 @@ extern "C" int ts_mha_decode_with_kvcache(const void* q, const void* k_cache, co
     return TS_MHA_ERR_LAUNCH;
   }
   return TS_MHA_OK;
+}
+
+}  // namespace
+
+extern "C" int ts_mha_decode_with_kvcache(const void* q, const void* k_cache, const void* v_cache,
+                                          const float* sinks, const int32_t* seqlens_k,
+                                          const int32_t* block_table, int32_t n_q_heads,
+                                          int32_t n_kv_heads, int32_t head_dim, int32_t window,
+                                          float softmax_scale, void* out, int32_t n_seqs,
+                                          int32_t n_pages, int32_t page_size, int32_t pages_per_seq,
+                                          int32_t max_seqlen_k, void* workspace,
+                                          int64_t workspace_bytes, void* stream) {
+  return decode_call(q, k_cache, v_cache, sinks, seqlens_k, block_table, n_q_heads, n_kv_heads, head_dim,
+                     window, softmax_scale, out, n_seqs, n_pages, page_size, pages_per_seq, max_seqlen_k,
+                     workspace, workspace_bytes, false, stream);
+}
+
+extern "C" int ts_mha_decode_with_kvcache_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                                  const float* sinks, const int32_t* seqlens_k,
+                                                  const int32_t* block_table, int32_t n_q_heads,
+                                                  int32_t n_kv_heads, int32_t head_dim, int32_t window,
+                                                  float softmax_scale, void* out, int32_t n_seqs,
+                                                  int32_t n_pages, int32_t page_size,
+                                                  int32_t pages_per_seq, int32_t max_seqlen_k,
+                                                  void* stream) {
+  return decode_call(q, k_cache, v_cache, sinks, seqlens_k, block_table, n_q_heads, n_kv_heads, head_dim,
+                     window, softmax_scale, out, n_seqs, n_pages, page_size, pages_per_seq, max_seqlen_k,
+                     nullptr, 0, true, stream);
 }
 
 extern "C" const char* ts_mha_strerror(int code) {
@@ -363,7 +433,8 @@ extern "C" const char* ts_mha_strerror(int code) {
       return "sequence lengths violate their contract (cu_seqlens: cu[0] == 0, non-decreasing, lengths <= "
              "max_seqlen; seqlens_k: 0 <= length <= max_seqlen_k)";
     case TS_MHA_ERR_WORKSPACE:
-      return "workspace missing or smaller than ts_mha_decode_workspace_size reports";
+      return "workspace missing or smaller than ts_mha_decode_workspace_size reports (noalloc decode: the "
+             "call needs more than the library's TS_MHA_NOALLOC_SCRATCH_BYTES of scratch)";
     case TS_MHA_ERR_PAGES: return "a block-table entry a sequence needs is outside [0, n_pages)";
     default: return "unknown error";
   }

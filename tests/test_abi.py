@@ -21,8 +21,9 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["ts_mha_decode_with_kvcache", "ts_mha_decode_workspace_size",
-                                    "ts_mha_prefill", "ts_mha_prefill_with_kvcache", "ts_mha_strerror",
+    assert declared_functions() == ["ts_mha_decode_with_kvcache", "ts_mha_decode_with_kvcache_noalloc",
+                                    "ts_mha_decode_workspace_size", "ts_mha_prefill",
+                                    "ts_mha_prefill_with_kvcache", "ts_mha_strerror",
                                     "ts_mha_unmasked_pairs"]
 
 
