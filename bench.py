@@ -20,7 +20,25 @@ i.e. 2*head_dim flops for q.k and 2*head_dim for the weighted sum of v, counted
 only on unmasked pairs.  Printed as one JSON line with a `roofline` object (the
 kernel's average duration from HIP events on the launch stream against the
 bf16 dense MFMA peak) and a `cpu_baseline` object (the fp64 oracle timed on
-this host's cores on a bounded row sample of the same workload).
+this host's cores on a bounded row sample of the same workload).  The line also
+carries:
+  per_launch        median / min / max of launches timed one by one, each between
+                    its own event pair (the pairs add their own gaps; the mean of
+                    the back-to-back launches above stays the figure);
+  roofline_valu     the vector ALU's roof: every visible score costs the softmax one
+                    v_mul_f32, one v_exp_f32 and half a v_cvt_pk_bf16_f32, and the
+                    microbenchmark (--ubench) gives the chip's rate of that mix at the
+                    kernel's occupancy; achieved = n_q_heads * visible pairs / kernel time;
+  mfma_sustained_tflops  the microbenchmark's back-to-back bf16 32x32x16 MFMA rate;
+  device            CU count and clocks from hipDeviceGetAttribute;
+  roofline_hbm, roofline_hbm_cold  (windowed workloads) algorithmic bytes over the
+                    kernel time, warm (back-to-back launches on resident inputs) and
+                    cold (the median of --cold-launches launches timed one by one,
+                    each after writing --flush-mib MiB of scratch, which leaves no
+                    line of the workload in the L2s or the last-level cache).
+
+    python bench.py --ubench   # issue rates of exp2, multiply, bf16 pack, the softmax
+                               # mix and the MFMA, and the device's CU count and clocks
 
 --decode times ts_mha_decode_with_kvcache on the paged-cache workloads: one step
 is one call (the split kernel and, for long sequences, the merge kernel), and the
@@ -164,6 +182,87 @@ def cpu_baseline(wl, inp, target_s: float):
                       f"fp64 oracle rows; {dt:.1f} s wall"}
 
 
+UBENCH_OPS = {"exp2": 0, "mul": 1, "cvt_pk_bf16": 2, "softmax_score": 3, "mfma_32x32x16_bf16": 4}
+
+
+def ubench_lib():
+    """The microbenchmark library (sinks_ts_mha_amd/libts_ubench.so), built beside libts_mha.so."""
+    import ctypes
+    path = os.path.join(ROOT, "sinks_ts_mha_amd", "libts_ubench.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build with `python -m sinks_ts_mha_amd.build`")
+    L = ctypes.CDLL(path)
+    ip = ctypes.POINTER(ctypes.c_int)
+    L.ts_ubench_device_info.argtypes = [ip, ip, ip, ip]
+    L.ts_ubench_device_info.restype = ctypes.c_int
+    L.ts_ubench_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.ts_ubench_valu.restype = ctypes.c_int
+    return L
+
+
+def device_info() -> dict:
+    """CU count and clocks of the current device, from hipDeviceGetAttribute."""
+    import ctypes
+    v = [ctypes.c_int(0) for _ in range(4)]
+    if ubench_lib().ts_ubench_device_info(*[ctypes.byref(x) for x in v]) != 0:
+        raise RuntimeError("hipDeviceGetAttribute failed")
+    return {"cus": v[0].value, "clock_mhz": v[1].value / 1000.0, "mem_clock_mhz": v[2].value / 1000.0,
+            "mem_bus_bits": v[3].value}
+
+
+def ubench_rates(names=None, target_ms: float = 8.0) -> dict:
+    """Issue rates of the microbenchmark kernels on every compute unit at two waves per SIMD
+    (two work-groups of four waves per CU): each lane runs 16 independent chains of the
+    instruction kind per loop trip.  Per kind: wave-level instructions per second, the SIMD
+    cycles one instruction takes at the device's reported clock, and for the softmax kind
+    the scores per second (one v_mul_f32, one v_exp_f32 and half a v_cvt_pk_bf16_f32 each),
+    for the MFMA kind the dense bf16 TFLOP/s (32768 flops per instruction)."""
+    import torch
+    L = ubench_lib()
+    info = device_info()
+    groups = 2 * info["cus"]
+    out = torch.empty(groups * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name in (names or UBENCH_OPS):
+        op = UBENCH_OPS[name]
+
+        def launch(iters):
+            if L.ts_ubench_valu(op, groups, iters, out.data_ptr(), stream.cuda_stream) != 0:
+                raise RuntimeError(f"microbenchmark {name} failed to launch")
+
+        iters = 256
+        for _ in range(8):  # size the launch for about target_ms
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch(iters)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            if ms >= target_ms / 2:
+                break
+            iters *= 2
+        times = []
+        for _ in range(7):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch(iters)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e-3)
+        t = sorted(times)[len(times) // 2]
+        insts = groups * 4 * iters * 16
+        r = {"wave_instructions_per_s": insts / t,
+             "simd_cycles_per_instruction": info["cus"] * 4 * info["clock_mhz"] * 1e6 * t / insts,
+             "median_launch_ms": round(t * 1e3, 3)}
+        if name == "softmax_score":
+            r["scores_per_s"] = insts * 64 / t
+        if name == "mfma_32x32x16_bf16":
+            r["tflops"] = insts * 32768 / t / 1e12
+        res[name] = r
+    return res
+
+
 def trace_summary(root: str, last: int):
     """Per-kernel durations from rocprofv3's kernel_trace.csv files under root: every dispatch,
     and the last `last` prefill dispatches (the timed region of a bench.py run)."""
@@ -228,6 +327,15 @@ def main():
                     help="time decode against a paged KV cache on its workloads instead")
     ap.add_argument("--prefill-kvcache", action="store_true",
                     help="time prefill of new rows against a paged KV cache instead")
+    ap.add_argument("--ubench", action="store_true",
+                    help="print the vector-ALU and MFMA issue rates of the microbenchmarks and the "
+                         "device's CU count and clocks instead")
+    ap.add_argument("--cold-launches", type=int, default=50,
+                    help="windowed workloads: launches timed one by one after writing --flush-mib "
+                         "of scratch memory each (the cold-cache figure)")
+    ap.add_argument("--flush-mib", type=int, default=512)
+    ap.add_argument("--per-launch", type=int, default=200,
+                    help="launches timed one by one (own event pair each) for the median and minimum")
     a = ap.parse_args()
     if a.trace_summary:
         trace_summary(a.trace_summary, a.steps)
@@ -246,9 +354,15 @@ def main():
     import sinks_ts_mha_amd as tm
     from sinks_ts_mha_amd import workloads
 
+    if a.ubench:
+        print(json.dumps({"device": device_info(), "ubench": ubench_rates()}), flush=True)
+        return
+
     dev = torch.device("cuda", 0)
     stream = torch.cuda.current_stream(dev)
     warm_counts = {}
+    per_launch = {}
+    cold_launch = {}
 
     def warm(fn) -> int:
         """At least --warmup launches and at least --warmup-seconds of them; returns the count."""
@@ -295,6 +409,29 @@ def main():
         ev1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        # The same launches timed one by one, each between its own event pair, for the
+        # median and minimum (the pairs add their own gaps, so the mean above stays the
+        # figure); with cold=True each is preceded by writing flush_mib of scratch, which
+        # leaves neither the L2s nor the last-level cache holding the workload's lines.
+        def one_by_one(n, cold):
+            flush = torch.empty(a.flush_mib << 20, dtype=torch.uint8, device=dev) if cold else None
+            pairs = []
+            for i in range(n):
+                if cold:
+                    flush.fill_(i & 0xff)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                step()
+                e1.record(stream)
+                pairs.append((e0, e1))
+            torch.cuda.synchronize()
+            ms = sorted(e0.elapsed_time(e1) for e0, e1 in pairs)
+            del flush
+            return {"median_us": round(ms[len(ms) // 2] * 1e3, 2), "min_us": round(ms[0] * 1e3, 2),
+                    "max_us": round(ms[-1] * 1e3, 2), "launches": n}
+        per_launch[wl.name] = one_by_one(min(steps, a.per_launch), False) if a.per_launch > 0 else None
+        if wl.window > 0 and a.cold_launches > 0:
+            cold_launch[wl.name] = one_by_one(a.cold_launches, True)
         ms_graph = None
         if graph_replay:
             # The same K launches captured in one HIP graph, replayed between one pair of
@@ -478,12 +615,30 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
     }
+    line["per_launch"] = per_launch.get(name)
+    # The vector ALU's roof: every visible score costs the softmax one v_mul_f32, one
+    # v_exp_f32 and half a v_cvt_pk_bf16_f32; the microbenchmark gives the chip's rate of
+    # exactly that mix at the kernel's occupancy.
+    rates = ubench_rates(["softmax_score", "mfma_32x32x16_bf16"])
+    scores = wl.n_q_heads * pairs
+    line["roofline_valu"] = {"bound": "valu", "achieved": round(scores / (avg_ms * 1e-3) / 1e9, 1),
+                             "peak": round(rates["softmax_score"]["scores_per_s"] / 1e9, 1),
+                             "unit": "Gscore/s",
+                             "frac": round(scores / (avg_ms * 1e-3) / rates["softmax_score"]["scores_per_s"], 4),
+                             "per_score": "v_mul_f32 + v_exp_f32 + 1/2 v_cvt_pk_bf16_f32"}
+    line["mfma_sustained_tflops"] = round(rates["mfma_32x32x16_bf16"]["tflops"], 1)
+    line["device"] = device_info()
     if wl.window > 0:
-        line["roofline_hbm"] = {"bound": "hbm",
-                                "achieved": round(algorithmic_bytes(wl) / (avg_ms * 1e-3) / 1e9, 1),
-                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                "frac": round(algorithmic_bytes(wl) / (avg_ms * 1e-3) / 1e9 /
-                                              PEAK_HBM_GBS, 4)}
+        gbs = algorithmic_bytes(wl) / (avg_ms * 1e-3) / 1e9
+        line["roofline_hbm"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "cache": "warm"}
+        cold = cold_launch.get(name)
+        if cold:
+            cgbs = algorithmic_bytes(wl) / (cold["median_us"] * 1e-6) / 1e9
+            line["roofline_hbm_cold"] = {"bound": "hbm", "achieved": round(cgbs, 1), "peak": PEAK_HBM_GBS,
+                                         "unit": "GB/s", "frac": round(cgbs / PEAK_HBM_GBS, 4),
+                                         "cache": f"cold: {a.flush_mib} MiB written before each launch",
+                                         **cold}
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, inp, a.cpu_seconds)
     print(json.dumps(line), flush=True)
