@@ -122,7 +122,11 @@ const char* ts_mha_strerror(int code);
  * ts_mha_unmasked_pairs -- number of visible (query, key) pairs per head, the
  * unit of the throughput metric: sum over sequences of L(L+1)/2 for full
  * causal, or W(W+1)/2 + (L-W)W when 0 < W < L.  Each pair costs 2*head_dim
- * flops for q.k and 2*head_dim for the weighted sum of v.
+ * flops for q.k and 2*head_dim for the weighted sum of v.  The metric is the
+ * prefill attention TFLOP/s of the chart in "TokenSpeed-kernel multi-silicon"
+ * (aixai.ru blog), section "Числа: Gluon на AMD MI355X" (full causal,
+ * head_dim 64, 64 query over 8 KV heads, sequence 1K-8K, batch 1-16); the
+ * page does not say how it counts flops, so masked pairs are not counted here.
  *
  *  cu_seqlens_host  host, int32 [n_seqs + 1], non-decreasing
  *  Returns the count, or -1 if cu_seqlens_host is NULL, n_seqs < 0 or a
