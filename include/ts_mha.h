@@ -60,8 +60,8 @@ extern "C" {
                                         head_dim 128: the rows of one work-group) or k/v rows
                                         ((max_seqlen + 64) * n_kv_heads * 2 * head_dim bytes)
                                         would exceed 2^31 - 1 */
-#define TS_MHA_ERR_UNSUPPORTED (-3)  /* head_dim not 64 (ts_mha_prefill: 64 or 128), or
-                                        n_q_heads / n_kv_heads not in {1,2,4,8,16} */
+#define TS_MHA_ERR_UNSUPPORTED (-3)  /* head_dim not 64 or 128, or n_q_heads / n_kv_heads
+                                        not in {1,2,4,8,16} */
 #define TS_MHA_ERR_BAD_SCALE (-4)    /* softmax_scale not finite or <= 0 */
 #define TS_MHA_ERR_ALIGN (-5)        /* q, k, v or out not 16-byte aligned; sinks or cu_seqlens not 4-byte aligned */
 #define TS_MHA_ERR_NO_DEVICE (-6)    /* no HIP device is present */
@@ -147,12 +147,13 @@ int64_t ts_mha_unmasked_pairs(const int32_t* cu_seqlens_host, int32_t n_seqs, in
  *    sequence's last q_len positions: row i sits at p = seqlens_k[b] - q_len + i
  *    (the causal diagonal aligned to the bottom right);
  *  - key position j lives in page block_table[b][j / page_size], slot
- *    j % page_size, of k_cache / v_cache [n_pages][page_size][n_kv_heads][64];
+ *    j % page_size, of k_cache / v_cache [n_pages][page_size][n_kv_heads][head_dim];
  *  - visible keys, sink, scale and head mapping are those of ts_mha_prefill at
  *    position p.  With q_len == seqlens_k[b] the result is ts_mha_prefill's.
  *
- *  q, out        device, bf16 [Tq][n_q_heads][64] packed by cu_seqlens_q, 16-byte
- *                aligned; out fully overwritten, no overlap with any input
+ *  q, out        device, bf16 [Tq][n_q_heads][head_dim] packed by cu_seqlens_q,
+ *                16-byte aligned; out fully overwritten, no overlap with any input
+ *  head_dim      64 or 128 (128 runs the 128-row prefill kernel's paged form)
  *  k_cache, v_cache, sinks, block_table, n_pages, page_size, pages_per_seq
  *                as for ts_mha_decode_with_kvcache
  *  cu_seqlens_q  device, int32 [n_seqs + 1]: cu[0] = 0, non-decreasing, each
@@ -186,14 +187,14 @@ int ts_mha_prefill_with_kvcache(const void* q, const void* k_cache, const void* 
  *    writes them first); seqlens_k[b] counts every cached key of sequence b,
  *    that one included, so the query sits at position p = seqlens_k[b] - 1;
  *  - key position j of sequence b lives in page block_table[b][j / page_size],
- *    slot j % page_size, of k_cache / v_cache [n_pages][page_size][n_kv_heads][64];
+ *    slot j % page_size, of k_cache / v_cache [n_pages][page_size][n_kv_heads][head_dim];
  *  - visible keys, sink, scale and the query-head to KV-head mapping are those
  *    of ts_mha_prefill at position p: keys j <= p with p - j < window when
  *    window > 0;
  *  - a sequence with seqlens_k[b] == 0 has no key and its output rows are zero.
  *
- *  q             device, bf16 [n_seqs][n_q_heads][64], 16-byte aligned
- *  k_cache, v_cache  device, bf16 [n_pages][page_size][n_kv_heads][64], 16-byte
+ *  q             device, bf16 [n_seqs][n_q_heads][head_dim], 16-byte aligned
+ *  k_cache, v_cache  device, bf16 [n_pages][page_size][n_kv_heads][head_dim], 16-byte
  *                aligned.  Slots no sequence uses (and slots at or past
  *                seqlens_k[b] in a sequence's last page) may hold anything,
  *                NaN included: they are never read.
@@ -203,7 +204,8 @@ int ts_mha_prefill_with_kvcache(const void* q, const void* k_cache, const void* 
  *                ceil(seqlens_k[b] / page_size) entries of row b are page ids in
  *                [0, n_pages); the rest are ignored
  *  n_q_heads, n_kv_heads, head_dim, window, softmax_scale   as for ts_mha_prefill
- *  out           device, bf16 [n_seqs][n_q_heads][64], 16-byte aligned, fully
+ *                (head_dim 64 or 128)
+ *  out           device, bf16 [n_seqs][n_q_heads][head_dim], 16-byte aligned, fully
  *                overwritten; must not overlap any input
  *  n_seqs        >= 0; 0 is a no-op
  *  n_pages       > 0, pages in the pool

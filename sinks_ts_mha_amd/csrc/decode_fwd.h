@@ -9,15 +9,16 @@
 namespace tsmha {
 
 struct DecodeArgs {
-  const void* q;              // bf16 [n_seqs][n_q_heads][64]
-  const void* k_cache;        // bf16 [n_pages][page_size][n_kv_heads][64]
-  const void* v_cache;        // bf16 [n_pages][page_size][n_kv_heads][64]
+  const void* q;              // bf16 [n_seqs][n_q_heads][head_dim]
+  const void* k_cache;        // bf16 [n_pages][page_size][n_kv_heads][head_dim]
+  const void* v_cache;        // bf16 [n_pages][page_size][n_kv_heads][head_dim]
   const float* sinks;         // fp32 [n_q_heads] or nullptr
   const int32_t* seqlens_k;   // int32 [n_seqs]
   const int32_t* block_table; // int32 [n_seqs][pages_per_seq]
-  void* out;                  // bf16 [n_seqs][n_q_heads][64]
+  void* out;                  // bf16 [n_seqs][n_q_heads][head_dim]
   int32_t n_q_heads;
   int32_t n_kv_heads;
+  int32_t head_dim;           // 64 or 128
   int32_t window;             // <= 0: none
   float softmax_scale;
   int32_t n_seqs;

@@ -53,18 +53,39 @@ namespace {
 
 using namespace cdna4;
 
-constexpr int kD = 64;                            // head_dim
-constexpr int kRowBytes = kD * 2;                 // one K or V row in bytes
 constexpr int kTileKeys = 32;                     // keys per LDS tile
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kStages = 4;                        // LDS tiles per wave, three in flight
-constexpr int kTileBytes = kTileKeys * kRowBytes;  // one tile of K (or V): 4 KiB
-constexpr int kLoads = kTileBytes / 1024;         // wave-wide loads per tile and operand
 constexpr int kChunkMax = 8192;                   // keys per work-group at most
 constexpr int kMinPage = 16;
 constexpr int kPageSlots = kChunkMax / kMinPage + 2;
 constexpr int kTargetGroups = 256;                // one work-group per CU
+
+// Sizes that follow from head_dim D (64 or 128).
+template <int D>
+struct DShape {
+  static constexpr int kRowBytes = 2 * D;                       // one K or V row
+  static constexpr int kChunks = kRowBytes / 16;                // 16-byte chunks per row
+  static constexpr int kTileBytes = kTileKeys * kRowBytes;      // one tile of K (or V)
+  static constexpr int kLoads = kTileBytes / 1024;              // wave-wide loads per tile and operand
+  static constexpr int kRowsPerLoad = 1024 / kRowBytes;
+  // LDS tiles per wave (kStages - 1 in flight): four at head_dim 64, two at 128,
+  // where four would not fit the LDS (4 waves x 2 x 8 KiB per stage)
+  static constexpr int kStages = D == 64 ? 4 : 2;
+  static constexpr int kKS = D / 32;                            // 32-wide steps of head_dim (scores)
+  static constexpr int kDB = D / 16;                            // 16-row blocks of O^T
+};
+
+// XOR key of row r in a tile: 128-byte rows use cdna4.h's key over 8 chunks;
+// 256-byte rows c ^ ((r & 3) << 2 | (r >> 2) & 3) over 16 chunks.  Either way
+// 16 consecutive rows reading one chunk (the K operand) and 4 aligned rows
+// reading two adjacent chunks (the V^T operand) hit distinct bank groups.
+template <int D>
+__device__ __forceinline__ int dkey(int row) {
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3); else return swz_key(row);
+}
+template <int D>
+__device__ __forceinline__ int dpos(int row, int ch) { return row * DShape<D>::kChunks + (ch ^ dkey<D>(row)); }
 
 struct DParams {
   const uint16_t* q;
@@ -75,8 +96,8 @@ struct DParams {
   const int32_t* block_table;
   uint16_t* out;
   float* ws_ml;          // [n_splits][n_seqs][Hq][2]: (m, l) of each chunk
-  float* ws_o;           // [n_splits][n_seqs][Hq][64]: unnormalised O of each chunk
-  int64_t page_elems;    // bf16 elements per page: page_size * n_kv_heads * 64
+  float* ws_o;           // [n_splits][n_seqs][Hq][D]: unnormalised O of each chunk
+  int64_t page_elems;    // bf16 elements per page: page_size * n_kv_heads * D
   int32_t page_bytes;
   int32_t n_kv_heads;
   int32_t n_seqs;
@@ -108,13 +129,20 @@ __device__ __forceinline__ float lane_group_sum(float x) {
 
 }  // namespace
 
-template <int G>
-__global__ void __launch_bounds__(kThreads, 1) decode_split_d64(DParams p) {
+template <int D, int G>
+__global__ void __launch_bounds__(kThreads, 1) decode_split(DParams p) {
   static_assert(G >= 1 && G <= 16, "the query heads of a KV head fill at most 16 MFMA columns");
-  __shared__ u32x4 ring[kWaves * kStages * 2 * kTileBytes / 16];  // [wave][stage][K, V][tile]
-  __shared__ float mo[kWaves][G][kD];                             // each wave's O
-  __shared__ float ml[kWaves][G][2];                              // each wave's (m, l)
-  __shared__ int pages[kPageSlots];                               // the chunk's page ids
+  using S = DShape<D>;
+  constexpr int kD = D;
+  constexpr int kRowBytes = S::kRowBytes;
+  constexpr int kTileBytes = S::kTileBytes;
+  constexpr int kLoads = S::kLoads;
+  constexpr int kStages = S::kStages;
+  constexpr int kWaveRing = kStages * 2 * kTileBytes;  // one wave's part of the ring
+  static_assert(G * D * 4 <= kWaveRing, "a wave's O fits its own part of the ring");
+  __shared__ u32x4 ring[kWaves * kWaveRing / 16];       // [wave][stage][K, V][tile]
+  __shared__ float ml[kWaves][G][2];                    // each wave's (m, l)
+  __shared__ int pages[kPageSlots];                     // the chunk's page ids
 
   const int Hkv = p.n_kv_heads;
   const int Hq = Hkv * G;
@@ -137,7 +165,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_split_d64(DParams p) {
     // No key in this chunk.  With one chunk per sequence the rows are written
     // here (a sequence without keys has zero output); otherwise decode_merge
     // skips the chunk.
-    if (p.n_splits == 1 && tid < G * 8)
+    if (p.n_splits == 1 && tid < G * kD / 8)
       *(u32x4*)(p.out + ((int64_t)b * Hq + g * G) * kD + tid * 8) = u32x4{0u, 0u, 0u, 0u};
     return;
   }
@@ -145,7 +173,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_split_d64(DParams p) {
   // ---- the chunk's page ids into LDS (clamped into the table and the pool, so
   // a malformed table cannot move a load outside the cache), and this lane's
   // query fragments: lane l holds head_dim elements 32 ks + 8 grp .. + 7 of
-  // query r16, the B operand of S^T = K Q^T.
+  // query r16 (ks < D / 32), the B operand of S^T = K Q^T.
   const int pidx0 = start >> p.page_shift;
   const int npg = min(((end - 1) >> p.page_shift) - pidx0 + 1, kPageSlots);
   {
@@ -155,14 +183,14 @@ __global__ void __launch_bounds__(kThreads, 1) decode_split_d64(DParams p) {
       pages[i] = min(max(pg, 0), p.n_pages - 1);
     }
   }
-  bf16x8 qf[2];
+  bf16x8 qf[S::kKS];
   if (r16 < G) {
     const uint16_t* qrow = p.q + ((int64_t)b * Hq + g * G + r16) * kD;
-    qf[0] = *(const bf16x8*)(qrow + 8 * grp);
-    qf[1] = *(const bf16x8*)(qrow + 32 + 8 * grp);
+#pragma unroll
+    for (int ks = 0; ks < S::kKS; ++ks) qf[ks] = *(const bf16x8*)(qrow + 32 * ks + 8 * grp);
   } else {
-    qf[0] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    qf[1] = qf[0];
+#pragma unroll
+    for (int ks = 0; ks < S::kKS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
   }
   float sink_t = -INFINITY;
   if (p.sinks && r16 < G) sink_t = p.sinks[g * G + r16] * kLog2e;
@@ -172,20 +200,21 @@ __global__ void __launch_bounds__(kThreads, 1) decode_split_d64(DParams p) {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // ---- tile loads.  The wave's i-th tile is the work-group's tile w + 4 i and
-  // goes to stage i % kStages.  Load `it` brings keys 8 it .. 8 it + 7 of the
-  // tile: lane l fetches 16 bytes of key 8 it + l / 8, placed at its swizzled
-  // chunk.  Loads past the wave's last tile still go out, with every lane out
-  // of range, so the number in flight is the same on every iteration.
+  // goes to stage i % kStages.  Load `it` brings the R = 1024 / (2 D) keys
+  // R it .. R it + R - 1 of the tile: lane l fetches 16 bytes of key
+  // R it + l / (D / 8), placed at its swizzled chunk.  Loads past the wave's
+  // last tile still go out, with every lane out of range, so the number in
+  // flight is the same on every iteration.
   const int nt = (end - start + kTileKeys - 1) / kTileKeys;
   const int my_tiles = nt > w ? (nt - w + kWaves - 1) / kWaves : 0;
   const int pmask = (1 << p.page_shift) - 1;
   int dch[kLoads];
 #pragma unroll
   for (int it = 0; it < kLoads; ++it) {
-    const int row = 8 * it + (lane >> 3);
-    dch[it] = ((lane & 7) ^ swz_key(row)) * 16 + g * kRowBytes;
+    const int row = S::kRowsPerLoad * it + lane / S::kChunks;
+    dch[it] = ((lane % S::kChunks) ^ dkey<D>(row)) * 16 + g * kRowBytes;
   }
-  const uint32_t ring_w = lds_addr(ring) + w * kStages * 2 * kTileBytes;
+  const uint32_t ring_w = lds_addr(ring) + w * kWaveRing;
   auto issue = [&](int i) {
     const int t = w + kWaves * i;
     const bool live = i < my_tiles;
@@ -200,9 +229,9 @@ __global__ void __launch_bounds__(kThreads, 1) decode_split_d64(DParams p) {
       const i32x4 rk = buffer_rsrc(p.kc + off, p.page_bytes);
       const i32x4 rv = buffer_rsrc(p.vc + off, p.page_bytes);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int it = 2 * half + j;
-        const int key = tile_key + 8 * it + (lane >> 3);
+      for (int j = 0; j < kLoads / 2; ++j) {
+        const int it = (kLoads / 2) * half + j;
+        const int key = tile_key + S::kRowsPerLoad * it + lane / S::kChunks;
         const int vo = (live && key < end) ? (key & pmask) * Hkv * kRowBytes + dch[it] : p.page_bytes;
         lds_dma16_nt(dk + it * 1024, rk, vo);
         lds_dma16_nt(dk + kTileBytes + it * 1024, rv, vo);
@@ -216,24 +245,24 @@ __global__ void __launch_bounds__(kThreads, 1) decode_split_d64(DParams p) {
   // grp read keys 4 grp + r16 / 4 (low half) and 16 more (high half), head_dim
   // columns 16 db + 4 (r16 % 4) .. + 3; the transpose hands lane r16 column
   // 16 db + r16 of those four keys.  Rows 16 apart share their swizzle key.
-  uint32_t voff[4];
+  uint32_t voff[S::kDB];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
+  for (int db = 0; db < S::kDB; ++db) {
     const int row = 4 * grp + (r16 >> 2);
     const int d = 16 * db + 4 * (r16 & 3);
-    voff[db] = row * kRowBytes + (((d >> 3) ^ swz_key(row)) << 4) + (d & 7) * 2;
+    voff[db] = row * kRowBytes + (((d >> 3) ^ dkey<D>(row)) << 4) + (d & 7) * 2;
   }
 
   float m = -INFINITY;  // running maximum of t for query r16 (identical across lane groups)
   float lsum = 0.f;     // this lane's share of the row sum
-  f32x4 o[4];           // O^T: element e of block db is head_dim 16 db + 4 grp + e, query r16
+  f32x4 o[S::kDB];      // O^T: element e of block db is head_dim 16 db + 4 grp + e, query r16
 #pragma unroll
-  for (int db = 0; db < 4; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < S::kDB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int i = 0; i < my_tiles; ++i) {
     issue(i + kStages - 1);
     wait_vmem<(kStages - 1) * 2 * kLoads>();  // tile i has landed
-    const lds_char* kt = (const lds_char*)ring + (w * kStages + i % kStages) * 2 * kTileBytes;
+    const lds_char* kt = (const lds_char*)ring + w * kWaveRing + (i % kStages) * 2 * kTileBytes;
     const lds_char* vt = kt + kTileBytes;
     const int tile_key = start + kTileKeys * (w + kWaves * i);
     const bool edge = tile_key < lo || tile_key + kTileKeys > L;
@@ -251,10 +280,12 @@ __global__ void __launch_bounds__(kThreads, 1) decode_split_d64(DParams p) {
           acc[e] = (key >= lo && key < L) ? 0.f : -INFINITY;
         }
       }
-      const bf16x8 k0 = *(const bf16x8*)(kt + swz(16 * kb + r16, grp) * 16);
-      const bf16x8 k1 = *(const bf16x8*)(kt + swz(16 * kb + r16, 4 + grp) * 16);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[0], acc, 0, 0, 0);
-      s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[1], acc, 0, 0, 0);
+#pragma unroll
+      for (int ks = 0; ks < S::kKS; ++ks) {
+        const bf16x8 kf = *(const bf16x8*)(kt + dpos<D>(16 * kb + r16, 4 * ks + grp) * 16);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], acc, 0, 0, 0);
+      }
+      s[kb] = acc;
     }
 
     // Streaming softmax of query r16 over the tile's 32 keys.
@@ -278,7 +309,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_split_d64(DParams p) {
 
     // O^T = alpha O^T + V^T P^T, the A operand's keys in P^T's order.
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < S::kDB; ++db) {
       const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + voff[db]));
       const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + voff[db] + 16 * kRowBytes));
       const u32x2 u0 = __builtin_bit_cast(u32x2, t0);
@@ -290,22 +321,27 @@ __global__ void __launch_bounds__(kThreads, 1) decode_split_d64(DParams p) {
   // The loads past the last tile land before the wave may leave its LDS.
   wait_vmem<0>();
 
-  // ---- combine the four waves.
+  // ---- combine the four waves.  Each wave's O goes into its own part of the
+  // ring, which nothing reads or loads into any more: the wave's own reads of
+  // it are done and its loads have landed.
+  auto mo = [&](int v, int q, int d) -> float& {
+    return reinterpret_cast<float*>(reinterpret_cast<char*>(ring) + v * kWaveRing)[q * kD + d];
+  };
   lsum = lane_group_sum(lsum);
   if (r16 < G) {
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < S::kDB; ++db)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) mo[w][r16][16 * db + 4 * grp + e] = o[db][e];
+      for (int e = 0; e < 4; ++e) mo(w, r16, 16 * db + 4 * grp + e) = o[db][e];
     if (grp == 0) {
       ml[w][r16][0] = m;
       ml[w][r16][1] = lsum;
     }
   }
   __syncthreads();
-  if (tid < G * 16) {
-    const int q = tid >> 4;
-    const int d0 = 4 * (tid & 15);
+  for (int idx = tid; idx < G * kD / 4; idx += kThreads) {
+    const int q = idx / (kD / 4);
+    const int d0 = 4 * (idx % (kD / 4));
     const int h = g * G + q;
     float M = -INFINITY;
 #pragma unroll
@@ -317,7 +353,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_split_d64(DParams p) {
       const float f = __builtin_amdgcn_exp2f(ml[v][q][0] - M);  // 0 for a wave without tiles
       lt = fmaf(f, ml[v][q][1], lt);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = fmaf(f, mo[v][q][d0 + e], acc[e]);
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(f, mo(v, q, d0 + e), acc[e]);
     }
     if (p.n_splits == 1) {
       const float st = __shfl(sink_t, q);  // lane q holds the sink of query q (wave 0)
@@ -344,9 +380,10 @@ __global__ void __launch_bounds__(kThreads, 1) decode_split_d64(DParams p) {
   }
 }
 
-// Combine the chunks of each (sequence, query head).  One work-group per
-// (sequence, query head): thread (sl, dc) folds chunks sl, sl + 16, ... of
-// head_dim elements 4 dc .. 4 dc + 3 into a running (m, l, O), the 16 chunk
+// Combine the chunks of each (sequence, query head).  One work-group of
+// 16 x D / 4 threads per (sequence, query head): thread (sl, dc) folds chunks
+// sl, sl + 16, ... of head_dim elements 4 dc .. 4 dc + 3 into a running
+// (m, l, O), the 16 chunk
 // lanes then combine by a butterfly, and the sink's term joins the
 // denominator.  The chunk loads of one thread are independent, so the loop
 // keeps several in flight.
@@ -363,7 +400,9 @@ __device__ __forceinline__ void fold(float& m, float& l, f32x4& o, float m2, flo
   m = mn;
 }
 
-__global__ void __launch_bounds__(256) decode_merge_d64(DParams p, int G) {
+template <int D>
+__global__ void __launch_bounds__(16 * D / 4) decode_merge(DParams p, int G) {
+  constexpr int kD = D;
   const int Hq = p.n_kv_heads * G;
   const int h = blockIdx.x % Hq;
   const int b = blockIdx.x / Hq;
@@ -399,14 +438,26 @@ __global__ void __launch_bounds__(256) decode_merge_d64(DParams p, int G) {
 
 namespace {
 
-template <int G>
+template <int D, int G>
 hipError_t launch_group(const DParams& kp, int64_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_d64<G>), dim3((unsigned)grid), dim3(kThreads), 0, stream, kp);
+  hipLaunchKernelGGL((decode_split<D, G>), dim3((unsigned)grid), dim3(kThreads), 0, stream, kp);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || kp.n_splits == 1) return err;
-  hipLaunchKernelGGL(decode_merge_d64, dim3((unsigned)(kp.n_seqs * kp.n_kv_heads * G)), dim3(256), 0,
+  hipLaunchKernelGGL(decode_merge<D>, dim3((unsigned)(kp.n_seqs * kp.n_kv_heads * G)), dim3(16 * D / 4), 0,
                      stream, kp, G);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const DParams& kp, int64_t grid, int G, hipStream_t stream) {
+  switch (G) {
+    case 1: return launch_group<D, 1>(kp, grid, stream);
+    case 2: return launch_group<D, 2>(kp, grid, stream);
+    case 4: return launch_group<D, 4>(kp, grid, stream);
+    case 8: return launch_group<D, 8>(kp, grid, stream);
+    case 16: return launch_group<D, 16>(kp, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
@@ -428,7 +479,7 @@ DecodePlan decode_plan(const DecodeArgs& a) {
   pl.n_splits = (int32_t)n_splits;
   if (n_splits > 1) {
     const int64_t rows = n_splits * a.n_seqs * (int64_t)a.n_q_heads;
-    pl.workspace_bytes = align_up(rows * 2 * 4, 256) + rows * kD * 4;
+    pl.workspace_bytes = align_up(rows * 2 * 4, 256) + rows * (int64_t)a.head_dim * 4;
   }
   return pl;
 }
@@ -449,8 +500,8 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, void* work
   kp.ws_o = plan.n_splits > 1
                 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(rows * 2 * 4, 256))
                 : nullptr;
-  kp.page_elems = (int64_t)a.page_size * a.n_kv_heads * kD;
-  kp.page_bytes = a.page_size * a.n_kv_heads * kRowBytes;
+  kp.page_elems = (int64_t)a.page_size * a.n_kv_heads * a.head_dim;
+  kp.page_bytes = a.page_size * a.n_kv_heads * 2 * a.head_dim;
   kp.n_kv_heads = a.n_kv_heads;
   kp.n_seqs = a.n_seqs;
   kp.n_pages = a.n_pages;
@@ -461,14 +512,9 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, void* work
   kp.n_splits = plan.n_splits;
   kp.c = a.softmax_scale * kLog2e;
   const int64_t grid = (int64_t)a.n_seqs * a.n_kv_heads * plan.n_splits;
-  switch (G) {
-    case 1: return launch_group<1>(kp, grid, stream);
-    case 2: return launch_group<2>(kp, grid, stream);
-    case 4: return launch_group<4>(kp, grid, stream);
-    case 8: return launch_group<8>(kp, grid, stream);
-    case 16: return launch_group<16>(kp, grid, stream);
-    default: return hipErrorInvalidValue;
-  }
+  if (a.head_dim == 128) return launch_d<128>(kp, grid, G, stream);
+  if (a.head_dim == 64) return launch_d<64>(kp, grid, G, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace tsmha

@@ -8,12 +8,12 @@
 namespace tsmha {
 
 struct PrefillArgs {
-  const void* q;             // bf16 [T][n_q_heads][64]
-  const void* k;             // bf16 [T][n_kv_heads][64], or the k cache (block_table set)
-  const void* v;             // bf16 [T][n_kv_heads][64], or the v cache
+  const void* q;             // bf16 [T][n_q_heads][head_dim]
+  const void* k;             // bf16 [T][n_kv_heads][head_dim], or the k cache (block_table set)
+  const void* v;             // bf16 [T][n_kv_heads][head_dim], or the v cache
   const float* sinks;        // fp32 [n_q_heads] or nullptr
   const int32_t* cu_seqlens; // int32 [n_seqs + 1], the new query rows
-  void* out;                 // bf16 [T][n_q_heads][64]
+  void* out;                 // bf16 [T][n_q_heads][head_dim]
   int32_t n_q_heads;
   int32_t n_kv_heads;
   int32_t window;            // <= 0: none
@@ -37,7 +37,8 @@ int64_t prefill_grid_size(const PrefillArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 // The same two calls for the 128-row work-groups of prefill_fwd_narrow.hip, at
-// head_dim 64 or 128 (packed K/V only: the grid size is -1 for a paged cache).
+// head_dim 64 or 128 (a paged cache at head_dim 128 only: the grid size is -1
+// for a paged cache at head_dim 64).
 int64_t prefill_grid_size_narrow(const PrefillArgs& a, int head_dim);
 hipError_t launch_prefill_narrow(const PrefillArgs& a, int head_dim, hipStream_t stream);
 

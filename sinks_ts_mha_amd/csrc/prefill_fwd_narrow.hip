@@ -36,6 +36,11 @@
 // transposed V reads) each hit distinct banks of the 64-bank LDS; 128-byte
 // rows use the swizzle of cdna4.h, laid out for the same access patterns.
 //
+// Paged K/V (head_dim 128 only; head_dim 64 uses the 256-row kernel's form):
+// the prefill of new rows against a cache, as in prefill_fwd.hip: query
+// positions shifted by the cached keys before them, each wave's 16 rows of a
+// tile loaded from one page.
+//
 // Softmax.  As in prefill_fwd.hip: base 2, scale * log2(e) applied to each fp32
 // score, every probability exp2 of its scaled score against reference 1,
 // row sums on the matrix pipe, and a streaming softmax with running maxima for
@@ -88,6 +93,14 @@ struct Params {
   int32_t n_pblocks;
   int32_t window;
   float c;  // softmax_scale * log2(e)
+  // paged K/V only: k and v are the caches [n_pages][page_size][n_kv_heads][D]
+  const int32_t* seqlens_k;    // cached keys per sequence, the new rows' own included
+  const int32_t* block_table;  // [n_seqs][pages_per_seq] page ids
+  int64_t page_elems;          // bf16 elements per page
+  int32_t page_bytes;
+  int32_t page_shift;
+  int32_t pages_per_seq;
+  int32_t n_pages;
 };
 
 // Position of 16-byte chunk `ch` of row `row` in a tile of 256-byte rows.
@@ -117,7 +130,7 @@ __device__ __forceinline__ float max16(const f32x16& a) {
   return fmaxf(fmaxf(x, a[14]), fmaxf(y, a[15]));
 }
 
-template <int D, int G, bool WINDOWED>
+template <int D, int G, bool WINDOWED, bool PAGED>
 __global__ void __launch_bounds__(kThreads, D == 64 ? 3 : 2) prefill_fwd_narrow(Params p) {
   using S = Shape<D>;
   constexpr int kD = D;
@@ -146,6 +159,10 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 3 : 2) prefill_fwd_narrow(
   const int L = p.cu[b + 1] - s;
   const int p0 = pblk * P;
   if (p0 >= L) return;
+  // With a KV cache the L new rows are the last L of the sequence's Lk cached
+  // positions: query row i sits at key position qoff + i.
+  const int Lk = PAGED ? p.seqlens_k[b] : L;
+  const int qoff = PAGED ? max(Lk - L, 0) : 0;
 
   __builtin_amdgcn_s_setprio(2);  // the prologue at raised priority, the walk at normal
   const int tid = threadIdx.x;
@@ -160,8 +177,8 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 3 : 2) prefill_fwd_narrow(
   float cv = p.c;
   asm volatile("" : "+v"(cv));
 
-  const int last = min(L, p0 + P) - 1;
-  const int first = WINDOWED ? max(0, p0 - p.window + 1) : 0;
+  const int last = qoff + min(L, p0 + P) - 1;
+  const int first = WINDOWED ? max(0, qoff + p0 - p.window + 1) : 0;
   const int kt0 = first / kBK;
   const int kt1 = last / kBK;
 
@@ -174,20 +191,52 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 3 : 2) prefill_fwd_narrow(
   const int tile_stride = kBK * Hkv * kRowBytes;
   const i32x4 rk = buffer_rsrc(p.k + seq_elems, nbytes);
   const i32x4 rv = buffer_rsrc(p.v + seq_elems, nbytes);
-  int voff[S::kTileLoads];
+  int voff[S::kTileLoads], pvoff[S::kTileLoads];
 #pragma unroll
   for (int i = 0; i < S::kTileLoads; ++i) {
     const int row = 16 * w + RPL * i + lane / kChunks;
     voff[i] = (row * Hkv + g) * kRowBytes + ((lane % kChunks) ^ tkey<D>(row)) * 16;
+    pvoff[i] = g * kRowBytes + ((lane % kChunks) ^ tkey<D>(row)) * 16;
   }
   const uint32_t lds_k_base = lds_addr(lds_k) + w * 16 * kRowBytes;
   const uint32_t lds_v_base = lds_addr(lds_v) + w * 16 * kRowBytes;
+  // Paged K/V: wave w loads rows 16 w .. 16 w + 15 of a tile, which lie in one
+  // page (pages hold at least 16 keys).  Lane l of pgv holds that page for
+  // tile pg_base - l; the walk only goes down, so the 64 ids are refilled when
+  // it leaves them (and when the exact redo restarts from the top).  Page ids
+  // are clamped into the table and the pool; keys at or past Lk read as zeros.
+  const int32_t* brow = PAGED ? p.block_table + (int64_t)b * p.pages_per_seq : nullptr;
+  const int pmask = PAGED ? (1 << p.page_shift) - 1 : 0;
+  int pg_base = -(1 << 30);
+  int pgv = 0;
+  auto tile_page = [&](int t) -> int {
+    if ((unsigned)(pg_base - t) >= 64u) {
+      pg_base = t;
+      const int tt = t - lane;
+      const int pi = tt >= 0 ? min((tt * kBK + 16 * w) >> p.page_shift, p.pages_per_seq - 1) : 0;
+      pgv = min(max(brow[pi], 0), p.n_pages - 1);
+    }
+    return __builtin_amdgcn_readlane(pgv, pg_base - t);
+  };
   auto issue_tile = [&](int t, int buf) {
-    const int off = t * tile_stride;
+    if constexpr (PAGED) {
+      const int64_t page_off = (int64_t)tile_page(t) * p.page_elems;
+      const i32x4 rkp = buffer_rsrc(p.k + page_off, p.page_bytes);
+      const i32x4 rvp = buffer_rsrc(p.v + page_off, p.page_bytes);
 #pragma unroll
-    for (int i = 0; i < S::kTileLoads; ++i) {
-      lds_dma16(lds_k_base + buf * kTileBytes + i * 1024, rk, off + voff[i]);
-      lds_dma16(lds_v_base + buf * kTileBytes + i * 1024, rv, off + voff[i]);
+      for (int i = 0; i < S::kTileLoads; ++i) {
+        const int key = t * kBK + 16 * w + RPL * i + lane / kChunks;
+        const int vo = key < Lk ? (key & pmask) * Hkv * kRowBytes + pvoff[i] : p.page_bytes;
+        lds_dma16(lds_k_base + buf * kTileBytes + i * 1024, rkp, vo);
+        lds_dma16(lds_v_base + buf * kTileBytes + i * 1024, rvp, vo);
+      }
+    } else {
+      const int off = t * tile_stride;
+#pragma unroll
+      for (int i = 0; i < S::kTileLoads; ++i) {
+        lds_dma16(lds_k_base + buf * kTileBytes + i * 1024, rk, off + voff[i]);
+        lds_dma16(lds_v_base + buf * kTileBytes + i * 1024, rv, off + voff[i]);
+      }
     }
   };
 
@@ -201,6 +250,13 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 3 : 2) prefill_fwd_narrow(
       __builtin_amdgcn_make_buffer_rsrc((void*)p.sinks, 0, p.sinks ? Hq * 4 : 0, kBufferConfig);
   const float sink_raw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsink, head * 4, 0, 0));
   auto sink_t = [&]() { return p.sinks ? sink_raw * kLog2e : -INFINITY; };
+
+  // The first tile's page id is looked up before any inline-assembly load is
+  // in flight (the compiler's wait for it would wait for those too).
+  if constexpr (PAGED) {
+    (void)tile_page(kt1);
+    asm volatile("" : : "v"(pgv));  // the wait for the ids stays ahead of those loads
+  }
 
   // The query rows go through slot 1 of the tiles (waves 0 and 1 in the K
   // slot, 2 and 3 in the V slot; 8 KiB each), with eight wave-wide loads of 4
@@ -264,7 +320,7 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 3 : 2) prefill_fwd_narrow(
     static_assert(WINDOWED || (M & kMaskWindow) == 0, "window mask without a window");
     f32x16 acc = {};
     if constexpr (M != 0) {
-      const int di = pos - k0 - 4 * hi;
+      const int di = qoff + pos - k0 - 4 * hi;
       // hidden <=> cc > di, or (with a window) cc <= di - window: the sign
       // bit of di - cc, or of cc - 1 - (di - window), selects the bits of
       // -inf, else 0.  Unsigned arithmetic: the second difference can pass
@@ -422,8 +478,8 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 3 : 2) prefill_fwd_narrow(
   // Walk the tiles from the last to the first; tiles [ktB, kt1] hold keys past
   // some row's position, tiles [kt0, ktA) keys that may have left some row's
   // window; only those take the mask, each run in a loop of its own.
-  const int ktB = max(kt0, min(kt1 + 1, (p0 + 1) / kBK));
-  const int xa = p0 + P - p.window;
+  const int ktB = max(kt0, min(kt1 + 1, (qoff + p0 + 1) / kBK));
+  const int xa = qoff + p0 + P - p.window;
   const int ktA = (WINDOWED && xa > 0) ? min(ktB, max(kt0, (xa + kBK - 1) / kBK)) : kt0;
   auto walk = [&](auto tile_fn, int kt_hi, int kt_lo) {
     for (int kt = kt_hi; kt >= kt_lo; --kt) {
@@ -556,22 +612,32 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 3 : 2) prefill_fwd_narrow(
 }
 
 template <int D, int G>
-hipError_t launch_g(const Params& kp, int64_t grid, bool windowed, hipStream_t stream) {
+hipError_t launch_g(const Params& kp, int64_t grid, bool windowed, bool paged, hipStream_t stream) {
   const dim3 gd((unsigned)grid), bd(kThreads);
+  if constexpr (D == 128) {  // head_dim 64 takes the 256-row kernel's paged form
+    if (paged) {
+      if (windowed)
+        hipLaunchKernelGGL((prefill_fwd_narrow<D, G, true, true>), gd, bd, 0, stream, kp);
+      else
+        hipLaunchKernelGGL((prefill_fwd_narrow<D, G, false, true>), gd, bd, 0, stream, kp);
+      return hipGetLastError();
+    }
+  }
+  if (paged) return hipErrorInvalidValue;
   if (windowed)
-    hipLaunchKernelGGL((prefill_fwd_narrow<D, G, true>), gd, bd, 0, stream, kp);
+    hipLaunchKernelGGL((prefill_fwd_narrow<D, G, true, false>), gd, bd, 0, stream, kp);
   else
-    hipLaunchKernelGGL((prefill_fwd_narrow<D, G, false>), gd, bd, 0, stream, kp);
+    hipLaunchKernelGGL((prefill_fwd_narrow<D, G, false, false>), gd, bd, 0, stream, kp);
   return hipGetLastError();
 }
 template <int D>
-hipError_t launch_d(const Params& kp, int64_t grid, int G, bool windowed, hipStream_t stream) {
+hipError_t launch_d(const Params& kp, int64_t grid, int G, bool windowed, bool paged, hipStream_t stream) {
   switch (G) {
-    case 1: return launch_g<D, 1>(kp, grid, windowed, stream);
-    case 2: return launch_g<D, 2>(kp, grid, windowed, stream);
-    case 4: return launch_g<D, 4>(kp, grid, windowed, stream);
-    case 8: return launch_g<D, 8>(kp, grid, windowed, stream);
-    case 16: return launch_g<D, 16>(kp, grid, windowed, stream);
+    case 1: return launch_g<D, 1>(kp, grid, windowed, paged, stream);
+    case 2: return launch_g<D, 2>(kp, grid, windowed, paged, stream);
+    case 4: return launch_g<D, 4>(kp, grid, windowed, paged, stream);
+    case 8: return launch_g<D, 8>(kp, grid, windowed, paged, stream);
+    case 16: return launch_g<D, 16>(kp, grid, windowed, paged, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -584,9 +650,11 @@ int64_t pblocks128(const PrefillArgs& a) {
 }  // namespace
 
 int64_t prefill_grid_size_narrow(const PrefillArgs& a, int head_dim) {
-  if (a.block_table) return -1;  // no paged form
+  if (a.block_table && head_dim != 128) return -1;  // the paged form is for head_dim 128
   const int64_t row_bytes = 2 * (int64_t)head_dim;
-  if (((int64_t)a.max_seqlen + kBK) * a.n_kv_heads * row_bytes > 0x7fffffffLL) return -1;
+  // each sequence's K (or V) rows must be addressable by one buffer descriptor
+  // (a cache is addressed page by page instead)
+  if (!a.block_table && ((int64_t)a.max_seqlen + kBK) * a.n_kv_heads * row_bytes > 0x7fffffffLL) return -1;
   if (((int64_t)a.max_seqlen + kRows) * a.n_q_heads * row_bytes > 0x7fffffffLL) return -1;
   const int64_t n = pblocks128(a) * (int64_t)a.n_seqs * (int64_t)a.n_kv_heads;
   if (n > 0x7fffffffLL) return -1;
@@ -608,10 +676,19 @@ hipError_t launch_prefill_narrow(const PrefillArgs& a, int head_dim, hipStream_t
   kp.n_pblocks = (int32_t)pblocks128(a);
   kp.window = a.window > 0 ? a.window : 0;
   kp.c = (float)((double)a.softmax_scale * 1.4426950408889634);
+  kp.seqlens_k = a.seqlens_k;
+  kp.block_table = a.block_table;
+  kp.page_elems = (int64_t)a.page_size * a.n_kv_heads * head_dim;
+  kp.page_bytes = a.page_size * a.n_kv_heads * 2 * head_dim;
+  kp.page_shift = a.page_size > 0 ? __builtin_ctz((unsigned)a.page_size) : 0;
+  kp.pages_per_seq = a.pages_per_seq;
+  kp.n_pages = a.n_pages;
   const bool windowed = a.window > 0;
+  const bool paged = a.block_table != nullptr;
   (void)hipGetLastError();
   const int G = a.n_q_heads / a.n_kv_heads;
-  return head_dim == 128 ? launch_d<128>(kp, grid, G, windowed, stream) : launch_d<64>(kp, grid, G, windowed, stream);
+  return head_dim == 128 ? launch_d<128>(kp, grid, G, windowed, paged, stream)
+                         : launch_d<64>(kp, grid, G, windowed, paged, stream);
 }
 
 }  // namespace tsmha

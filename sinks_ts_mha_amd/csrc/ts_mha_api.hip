@@ -145,17 +145,18 @@ int check_cache_shapes(int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, 
   if (max_seqlen_k > (1 << 30) || (int64_t)max_seqlen_k > (int64_t)pages_per_seq * page_size)
     return TS_MHA_ERR_BAD_SHAPE;
   const int32_t G = n_q_heads / n_kv_heads;
-  if (head_dim != 64) return TS_MHA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return TS_MHA_ERR_UNSUPPORTED;
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return TS_MHA_ERR_UNSUPPORTED;
   if (!isfinite(softmax_scale) || !(softmax_scale > 0.f)) return TS_MHA_ERR_BAD_SCALE;
   return TS_MHA_OK;
 }
 
-tsmha::DecodeArgs decode_args(int32_t n_q_heads, int32_t n_kv_heads, int32_t window, int32_t n_seqs,
-                              int32_t max_seqlen_k) {
+tsmha::DecodeArgs decode_args(int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t window,
+                              int32_t n_seqs, int32_t max_seqlen_k) {
   tsmha::DecodeArgs a{};
   a.n_q_heads = n_q_heads;
   a.n_kv_heads = n_kv_heads;
+  a.head_dim = head_dim;
   a.window = window;
   a.n_seqs = n_seqs;
   a.max_seqlen_k = max_seqlen_k;
@@ -265,7 +266,8 @@ extern "C" int ts_mha_prefill_with_kvcache(const void* q, const void* k_cache, c
   a.n_pages = n_pages;
   a.page_size = page_size;
   a.pages_per_seq = pages_per_seq;
-  const int64_t grid = tsmha::prefill_grid_size(a);
+  // head_dim 64: the 256-row kernel's paged form; head_dim 128: the 128-row kernel's
+  const int64_t grid = head_dim == 64 ? tsmha::prefill_grid_size(a) : tsmha::prefill_grid_size_narrow(a, head_dim);
   if (grid < 0) return TS_MHA_ERR_BAD_SHAPE;
 
   rc = check_device();
@@ -280,7 +282,7 @@ extern "C" int ts_mha_prefill_with_kvcache(const void* q, const void* k_cache, c
     if (rc != TS_MHA_OK) return rc;
   }
   if (grid == 0) return TS_MHA_OK;
-  const hipError_t err = tsmha::launch_prefill(a, st);
+  const hipError_t err = head_dim == 64 ? tsmha::launch_prefill(a, st) : tsmha::launch_prefill_narrow(a, head_dim, st);
   if (err != hipSuccess) {
     snprintf(g_launch_msg, sizeof g_launch_msg, "%s", hipGetErrorString(err));
     return TS_MHA_ERR_LAUNCH;
@@ -293,7 +295,7 @@ extern "C" int64_t ts_mha_decode_workspace_size(int32_t n_seqs, int32_t n_q_head
   const int rc = check_cache_shapes(n_q_heads, n_kv_heads, head_dim, 1.f, n_seqs, 1, 16,
                                     (max_seqlen_k + 15) / 16 + 1, max_seqlen_k);
   if (rc != TS_MHA_OK) return rc;
-  const tsmha::DecodePlan plan = tsmha::decode_plan(decode_args(n_q_heads, n_kv_heads, window, n_seqs, max_seqlen_k));
+  const tsmha::DecodePlan plan = tsmha::decode_plan(decode_args(n_q_heads, n_kv_heads, head_dim, window, n_seqs, max_seqlen_k));
   if (plan.n_splits < 0) return TS_MHA_ERR_BAD_SHAPE;
   return plan.workspace_bytes;
 }
@@ -337,7 +339,7 @@ int decode_call(const void* q, const void* k_cache, const void* v_cache, const f
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
       !aligned(sinks, 4) || !aligned(seqlens_k, 4) || !aligned(block_table, 4) || !aligned(workspace, 256))
     return TS_MHA_ERR_ALIGN;
-  tsmha::DecodeArgs a = decode_args(n_q_heads, n_kv_heads, window, n_seqs, max_seqlen_k);
+  tsmha::DecodeArgs a = decode_args(n_q_heads, n_kv_heads, head_dim, window, n_seqs, max_seqlen_k);
   a.q = q;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
@@ -416,8 +418,8 @@ extern "C" const char* ts_mha_strerror(int code) {
              "max_seqlen must be >= 0, the launch grid must fit; for the cache calls page_size a power "
              "of two >= 16, n_pages and pages_per_seq > 0, max_seqlen_k <= pages_per_seq * page_size";
     case TS_MHA_ERR_UNSUPPORTED:
-      return "unsupported configuration: head_dim must be 64 (or 128 for ts_mha_prefill) and "
-             "n_q_heads / n_kv_heads one of 1, 2, 4, 8, 16";
+      return "unsupported configuration: head_dim must be 64 or 128 and n_q_heads / n_kv_heads one of "
+             "1, 2, 4, 8, 16";
     case TS_MHA_ERR_BAD_SCALE: return "softmax_scale must be finite and > 0";
     case TS_MHA_ERR_ALIGN:
       return "misaligned pointer: q, k, v (or the caches), out need 16-byte alignment, sinks, "

@@ -218,6 +218,9 @@ DECODE_WORKLOADS = {
     "decode_b1_k65536": decode(
         (65536,), name="decode_b1_k65536",
         notes="one long sequence, decode: 65536 cached keys, page 16, sinks"),
+    "decode_d128_b64_k8192": decode(
+        (8192,) * 64, name="decode_d128_b64_k8192", head_dim=128, softmax_scale=128 ** -0.5,
+        notes="head_dim 128, decode: 64 sequences x 8192 cached keys, 64 q / 8 KV heads, page 16, sinks"),
 }
 
 
@@ -230,6 +233,10 @@ PREFILL_KV_WORKLOADS = {
     "prefill_kv_b4_q2048_k8192_window128": CacheWorkload(
         "prefill_kv_b4_q2048_k8192_window128", (2048,) * 4, (8192,) * 4, 64, 8, page_size=16,
         window=128, notes="chunked prefill, window-128 layer: 4 x 2048 new rows, 8192 cached keys"),
+    "prefill_kv_d128_b4_q2048_k8192": CacheWorkload(
+        "prefill_kv_d128_b4_q2048_k8192", (2048,) * 4, (8192,) * 4, 64, 8, page_size=16, head_dim=128,
+        softmax_scale=128 ** -0.5,
+        notes="head_dim 128 chunked prefill: 4 sequences x 2048 new rows against 8192 cached keys"),
 }
 
 CACHE_WORKLOADS = {**DECODE_WORKLOADS, **PREFILL_KV_WORKLOADS}

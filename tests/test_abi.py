@@ -160,7 +160,7 @@ def dcall(q=FAKE, kc=FAKE, vc=FAKE, sinks=None, lens=FAKE, table=FAKE, hq=64, hk
     (dict(hq=0), -2), (dict(hq=12, hkv=8), -2), (dict(n_seqs=-1), -2), (dict(max_k=-1), -2),
     (dict(n_pages=0), -2), (dict(pps=0), -2), (dict(page=8), -2), (dict(page=24), -2),
     (dict(page=0), -2), (dict(max_k=512 * 16 + 1), -2), (dict(page=1 << 20, hkv=64, hq=64), -2),
-    (dict(d=128), -3), (dict(hq=64, hkv=2), -3),
+    (dict(d=96), -3), (dict(d=256), -3), (dict(hq=64, hkv=2), -3),
     (dict(scale=0.0), -4), (dict(scale=float("nan")), -4),
     (dict(q=FAKE + 8), -5), (dict(kc=FAKE + 4), -5), (dict(out=FAKE + 2), -5),
     (dict(table=FAKE + 2), -5), (dict(ws=FAKE + 64), -5),
@@ -180,8 +180,11 @@ def test_decode_workspace_size():
     assert big > 0 and big % 4 == 0
     assert ws(1, 64, 8, 64, 0, 65536) == big  # a function of its arguments only
     assert ws(0, 64, 8, 64, 0, 0) == 0
+    # head_dim 128: the same split, twice the partial output per row
+    d128 = ws(1, 64, 8, 128, 0, 65536)
+    assert d128 > big and (d128 - big) % (64 * 4) == 0
     with pytest.raises(tm.TsMhaError):
-        ws(1, 64, 8, 128, 0, 1024)
+        ws(1, 64, 8, 96, 0, 1024)
     with pytest.raises(tm.TsMhaError):
         ws(1, 12, 8, 64, 0, 1024)
 
@@ -193,6 +196,7 @@ def test_decode_validation_precedes_device_check():
     assert dcall(n_seqs=0) == -6
     assert dcall(n_seqs=1, max_k=65536, pps=4096, ws_bytes=1 << 30) == -6
     assert dcall(ws=None, max_k=2048, n_seqs=256) == -6  # no workspace needed there
+    assert dcall(d=128) == -6 and dcall(d=128, n_seqs=1, max_k=65536, pps=4096, ws_bytes=1 << 30) == -6
 
 
 # ---- prefill of new rows against a paged KV cache
@@ -213,7 +217,7 @@ def pcall(q=FAKE, kc=FAKE, vc=FAKE, sinks=None, cu=FAKE, lens=FAKE, table=FAKE, 
     (dict(pps=0), -2), (dict(max_k=512 * 16 + 1), -2),
     # one sequence's q rows beyond 2^31 - 1 bytes
     (dict(max_q=262000, max_k=262000, pps=16384, n_seqs=1), -2),
-    (dict(d=128), -3), (dict(hq=64, hkv=2), -3),
+    (dict(d=96), -3), (dict(d=256), -3), (dict(hq=64, hkv=2), -3),
     (dict(scale=0.0), -4), (dict(scale=float("inf")), -4),
     (dict(q=FAKE + 8), -5), (dict(vc=FAKE + 4), -5), (dict(out=FAKE + 2), -5), (dict(cu=FAKE + 2), -5),
     (dict(lens=FAKE + 1), -5),
@@ -228,3 +232,4 @@ def test_prefill_kvcache_validation_precedes_device_check():
     assert pcall() == -6
     assert pcall(n_seqs=0, max_q=0, max_k=0) == -6
     assert pcall(window=128, sinks=FAKE) == -6
+    assert pcall(d=128) == -6 and pcall(d=128, window=128, page=64) == -6
