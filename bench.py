@@ -272,18 +272,39 @@ def trace_summary(root: str, last: int):
     for path in glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True):
         with open(path) as f:
             for r in csv.DictReader(f):
+                grid = r.get("Grid_Size_X") or r.get("Grid_Size") or "0"
                 rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),
-                             r["Kernel_Name"]))
+                             r["Kernel_Name"], int(grid)))
     rows.sort()
-    names = sorted({n for _, _, n in rows})
+    names = sorted({n for _, _, n, _ in rows})
     print(f"{'kernel':70s} {'calls':>6s} {'avg_ns':>12s} {'min_ns':>10s} {'max_ns':>10s}")
     for n in names:
-        d = [x for _, x, k in rows if k == n]
+        d = [x for _, x, k, _ in rows if k == n]
         print(f"{n[:70]:70s} {len(d):6d} {sum(d) / len(d):12.1f} {min(d):10d} {max(d):10d}")
-    d = [x for _, x, k in rows if "prefill_fwd" in k][-last:]
+    d = [x for _, x, k, _ in rows if "prefill_fwd" in k][-last:]
     if d:
         print(f"timed region (last {len(d)} prefill dispatches): avg_ns {sum(d) / len(d):.1f} "
               f"min_ns {min(d)} max_ns {max(d)}")
+    # Phases: the dispatches of one kernel with one grid size in a row (other kernels' dispatches
+    # in between do not break a phase; a grid change or a pause of over 20 ms does), i.e. the
+    # warm-up and timed launches of one workload; the average is over the phase's last `last`.
+    print(f"phases (per kernel: runs of one grid size, split at pauses over 20 ms; avg and min of the last "
+          f"{last} dispatches of each):")
+    print(f"{'#':>3s} {'kernel':60s} {'grid':>9s} {'calls':>6s} {'avg_ns':>12s} {'min_ns':>10s}")
+    phases = []
+    for n in names:
+        cur = None
+        for t, x, k, g in rows:
+            if k != n:
+                continue
+            if cur is None or g != cur["grid"] or t - cur["end"] > 20_000_000:
+                cur = {"name": n, "grid": g, "start": t, "end": t + x, "d": []}
+                phases.append(cur)
+            cur["d"].append(x)
+            cur["end"] = t + x
+    for i, ph in enumerate(sorted(phases, key=lambda p: p["start"])):
+        d = ph["d"][-last:]
+        print(f"{i:3d} {ph['name'][:60]:60s} {ph['grid']:9d} {len(ph['d']):6d} {sum(d) / len(d):12.1f} {min(d):10d}")
 
 
 def counter_summary(root: str):

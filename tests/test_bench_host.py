@@ -85,3 +85,22 @@ def test_counter_summary_sums_instances_per_dispatch(tmp_path, capsys):
     line = [l for l in capsys.readouterr().out.splitlines() if "FETCH_SIZE" in l][0]
     parts = line.split()
     assert parts[-2] == "2" and float(parts[-1]) == pytest.approx(50.0)
+
+
+def test_trace_summary_phases(tmp_path, capsys):
+    """Phases split one kernel's dispatches at a grid change or a pause over 20 ms; another
+    kernel's dispatches in between (a merge kernel after each split) do not split them."""
+    rows = ["Kernel_Name,Start_Timestamp,End_Timestamp,Grid_Size_X"]
+    t = 0
+    for grid, durs in ((512, (500, 100, 100)), (512, (700, 300, 300)), (256, (50, 40))):
+        t += 30_000_000  # a pause between workloads
+        for dur in durs:
+            rows.append(f"split,{t},{t + dur},{grid}")
+            rows.append(f"merge,{t + dur},{t + dur + 5},64")
+            t += 1000
+    (tmp_path / "y_kernel_trace.csv").write_text("\n".join(rows) + "\n")
+    bench.trace_summary(str(tmp_path), 2)
+    lines = [l.split() for l in capsys.readouterr().out.splitlines() if l[:3].strip().isdigit()]
+    split = [(int(l[2]), int(l[3]), float(l[4])) for l in lines if l[1] == "split"]
+    assert split == [(512, 3, 100.0), (512, 3, 300.0), (256, 2, 45.0)]
+    assert sum(1 for l in lines if l[1] == "merge") == 3
