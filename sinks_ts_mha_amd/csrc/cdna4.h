@@ -99,6 +99,24 @@ __device__ __forceinline__ bool positive_in_binade_range(float x, int lo, int hi
   return e >= lo && e <= hi;
 }
 
+// Sum of the 32 elements of two 16-wide vectors in a fixed pairwise order (a
+// dependency chain of 5 additions instead of 31); the prefill kernels use it
+// for the same 32 accumulator values of a row block, so both sum alike.
+template <typename V16>
+__device__ __forceinline__ float pairwise_sum32(const V16& a, const V16& b) {
+  float t[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    t[i] = a[2 * i] + a[2 * i + 1];
+    t[8 + i] = b[2 * i] + b[2 * i + 1];
+  }
+#pragma unroll
+  for (int n = 8; n >= 1; n >>= 1)
+#pragma unroll
+    for (int i = 0; i < n; ++i) t[i] = t[2 * i] + t[2 * i + 1];
+  return t[0];
+}
+
 // Position of 16-byte chunk `ch` of row `row` (8 chunks of a 128-byte row) in
 // an LDS tile.  The LDS serves 64 banks of 4 bytes per cycle, two 128-byte
 // rows; the XOR key (row bit 1 as chunk bit 2, row bits 2..3 as chunk bits

@@ -636,11 +636,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
     bool bad = false;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      float osum = 0.f;
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) osum += o[db][nb][e];
+      const float osum = pairwise_sum32(o[0][nb], o[1][nb]);
       bad = bad || !positive_in_binade_range(lrow[nb], -kFastSumBinades, kFastSumBinades) ||
             !finite_bits(osum);
     }
@@ -671,7 +667,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
     for (int nb = 0; nb < 2; ++nb) {
       float lt = lrow[nb];
       if (p.sinks) lt += __builtin_amdgcn_exp2f(sink_t(nb) - mref[nb]);
-      const float inv = 1.f / lt;
+      const float inv = __builtin_amdgcn_rcpf(lt);  // v_rcp_f32: 1 ulp, far below the bf16 rounding
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll

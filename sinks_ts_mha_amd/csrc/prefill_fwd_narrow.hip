@@ -552,11 +552,8 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 3 : 2) prefill_fwd_narrow(
   // The fast pass is kept unless a row's sum left [2^-64, 2^65) or a sum or an
   // output is not finite; then the work-group redoes its rows exactly.
   {
-    float osum = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) osum += o[db][e];
+    float osum = pairwise_sum32(o[0], o[1]);
+    if constexpr (DB == 4) osum += pairwise_sum32(o[2], o[3]);
     const bool bad = !positive_in_binade_range(lrow, -kFastSumBinades, kFastSumBinades) || !finite_bits(osum);
     const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
     if (lane == 0) redo_vote[w] = wave_bad ? 1 : 0;
@@ -586,7 +583,7 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 3 : 2) prefill_fwd_narrow(
   lds_char* const ob = (w < 2 ? (lds_char*)lds_k : (lds_char*)lds_v) + free_slot * kTileBytes + (w & 1) * kQW * kRowBytes;
   float lt = lrow;
   if (p.sinks) lt += __builtin_amdgcn_exp2f(sink_t() - mref);
-  const float inv = 1.f / lt;
+  const float inv = __builtin_amdgcn_rcpf(lt);  // v_rcp_f32: 1 ulp, far below the bf16 rounding
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
