@@ -117,6 +117,93 @@ __device__ __forceinline__ float pairwise_sum32(const V16& a, const V16& b) {
   return t[0];
 }
 
+// Work items of a grid of position blocks over packed sequences with the
+// blocks that lie past their sequence's end left out.  A grid sized from the
+// longest sequence holds a work-group for each such block, and under load each
+// of them holds a compute unit's slot far longer than its few instructions, so
+// when many blocks are empty the kernels compact the order instead (the grid
+// keeps its size; its surplus ids come last and return at once).  Sequence b,
+// rows cu[b] .. cu[b+1] - 1, has n_b = min(ceil(L_b / U), n_levels) blocks of
+// U positions.  One lane per sequence (n_seqs <= 64): c0 = cu[lane] and
+// c1 = cu[lane + 1] on lanes below n_seqs, 0 elsewhere.  All lanes of the wave
+// call these, and get the same wave-uniform result: block `blk` of sequence
+// `seq`, whose rows start at `start` and number `len`; false when item j is
+// past the last one.
+constexpr int kCompactMaxSeqs = 64;
+struct BlockItem {
+  int seq, blk, start, len;
+};
+extern "C" __device__ int __ockl_wfred_add_i32(int);
+
+__device__ __forceinline__ int lane_id() {
+  return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+__device__ __forceinline__ void fill_block_item(int seq, int blk, int c0, int c1, BlockItem& it) {
+  it.seq = seq;
+  it.blk = blk;
+  it.start = __builtin_amdgcn_readlane(c0, seq);
+  it.len = __builtin_amdgcn_readlane(c1, seq) - it.start;
+}
+
+// Inclusive prefix sum over the 64 lanes: sums within rows of 16 lanes by
+// shifts of 1, 2, 4 and 8, then row 0's total into row 1 and row 2's into
+// row 3, then the total of rows 0-1 into rows 2-3 (DPP row broadcasts).
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
+// Sequence-major order: the blocks of sequence 0 first, then those of
+// sequence 1, and so on, ascending within a sequence (one prefix sum).
+__device__ __forceinline__ bool block_item_by_sequence(int n_seqs, int U, int n_levels, int j, int c0, int c1,
+                                                       BlockItem& it) {
+  const int nb = lane_id() < n_seqs ? min((c1 - c0 + U - 1) / U, n_levels) : 0;
+  const int incl = wave_inclusive_sum(nb);
+  if (j >= __builtin_amdgcn_readlane(incl, 63)) return false;
+  // the sequences whose blocks all come before item j are the first lanes
+  const int seq = __builtin_popcountll(__builtin_amdgcn_ballot_w64(incl <= j));
+  fill_block_item(seq, j - (__builtin_amdgcn_readlane(incl, seq) - __builtin_amdgcn_readlane(nb, seq)), c0, c1, it);
+  return true;
+}
+
+// Level-major order: block index from the last level down to 0 (under a
+// causal mask the late blocks carry the most work, so it starts first), by
+// sequence within a level; a binary search over levels, each step one wave sum.
+__device__ __forceinline__ bool block_item_by_level(int n_seqs, int U, int n_levels, int j, int c0, int c1,
+                                                    BlockItem& it) {
+  const int nb = lane_id() < n_seqs ? min((c1 - c0 + U - 1) / U, n_levels) : 0;
+  auto at_or_above = [&](int k) { return __ockl_wfred_add_i32(max(nb - k, 0)); };  // items at levels >= k
+  if (j >= at_or_above(0)) return false;
+  int lo = 0, hi = n_levels - 1;  // the item's level: the largest k with at_or_above(k) > j
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (at_or_above(mid) > j) lo = mid;
+    else hi = mid - 1;
+  }
+  const int r = j - at_or_above(lo + 1);  // its rank among the sequences that reach level lo
+  const bool active = nb > lo;
+  const uint64_t act = __builtin_amdgcn_ballot_w64(active);
+  const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(act >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)act, 0u));
+  const uint64_t hit = __builtin_amdgcn_ballot_w64(active && below == r);
+  if (hit == 0) return false;
+  fill_block_item(__builtin_ctzll(hit), lo, c0, c1, it);
+  return true;
+}
+
+// Whether a launch compacts its order: up to kCompactMaxSeqs sequences, and
+// at least a fifth of the grid's blocks empty (total rows T against
+// n_seqs * max_seqlen; a fuller grid loses less to its empty blocks than the
+// search costs every work-group).
+__device__ __forceinline__ bool compact_grid(int n_seqs, int total_rows, int max_seqlen) {
+  return n_seqs <= kCompactMaxSeqs && 5LL * total_rows < 4LL * n_seqs * max_seqlen;
+}
+
 // Position of 16-byte chunk `ch` of row `row` (8 chunks of a 128-byte row) in
 // an LDS tile.  The LDS serves 64 banks of 4 bytes per cycle, two 128-byte
 // rows; the XOR key (row bit 1 as chunk bit 2, row bits 2..3 as chunk bits

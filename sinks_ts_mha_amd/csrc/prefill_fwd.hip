@@ -117,6 +117,7 @@ struct KParams {
   int32_t page_shift;
   int32_t pages_per_seq;
   int32_t n_pages;
+  int32_t max_seqlen;
 };
 
 namespace {
@@ -159,13 +160,33 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   // Consecutive work-group ids go to different XCDs; with the KV head as the
   // fastest index, each XCD's L2 sees the K/V of a fixed set of heads.
   const int g = id % Hkv;
-  const int rest = id / Hkv;
-  const int b = rest % p.n_seqs;
+  const int item = id / Hkv;
   // Position blocks are issued last-first: under a causal mask the late blocks
-  // carry the most key tiles, so the longest work starts first.
-  const int pblk = p.n_pblocks - 1 - rest / p.n_seqs;
-  const int s = p.cu[b];
-  const int L = p.cu[b + 1] - s;
+  // carry the most key tiles, so the longest work starts first.  When many
+  // blocks lie past their sequence's end (the grid is sized for the longest
+  // sequence) the order leaves them out, and its surplus ids come last and
+  // return at once; a windowed layer's blocks all carry about the same work,
+  // so its order only keeps a sequence's blocks together (their K/V tiles
+  // overlap).
+  int b = item % p.n_seqs;
+  int pblk = p.n_pblocks - 1 - item / p.n_seqs;
+  int s = p.cu[b];
+  int L = p.cu[b + 1] - s;
+  if (compact_grid(p.n_seqs, p.cu[p.n_seqs], p.max_seqlen)) {
+    int c0 = 0, c1 = 0;
+    if (lane_id() < p.n_seqs) {
+      c0 = p.cu[lane_id()];
+      c1 = p.cu[lane_id() + 1];
+    }
+    BlockItem bi;
+    const bool found = WINDOWED ? block_item_by_sequence(p.n_seqs, P, p.n_pblocks, item, c0, c1, bi)
+                                : block_item_by_level(p.n_seqs, P, p.n_pblocks, item, c0, c1, bi);
+    if (!found) return;
+    b = bi.seq;
+    pblk = bi.blk;
+    s = bi.start;
+    L = bi.len;
+  }
   const int p0 = pblk * P;
   if (p0 >= L) return;
   // With a KV cache the L new rows are the last L of the sequence's Lk cached
@@ -767,6 +788,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   kp.page_shift = a.page_size > 0 ? __builtin_ctz((unsigned)a.page_size) : 0;
   kp.pages_per_seq = a.pages_per_seq;
   kp.n_pages = a.n_pages;
+  kp.max_seqlen = a.max_seqlen;
   const bool windowed = a.window > 0;
   const bool paged = a.block_table != nullptr;
   (void)hipGetLastError();  // start from a clean per-thread error state

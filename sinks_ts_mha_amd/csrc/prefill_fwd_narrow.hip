@@ -91,6 +91,7 @@ struct Params {
   int32_t n_kv_heads;
   int32_t n_seqs;
   int32_t n_pblocks;
+  int32_t max_seqlen;
   int32_t window;
   float c;  // softmax_scale * log2(e)
   // paged K/V only: k and v are the caches [n_pages][page_size][n_kv_heads][D]
@@ -150,13 +151,29 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 3 : 2) prefill_fwd_narrow(
   const int Hq = Hkv * G;
   const int id = blockIdx.x;
   // KV head fastest (each XCD's L2 serves a fixed set of heads), position
-  // blocks last-first (the longest causal work starts first).
+  // blocks last-first (the longest causal work starts first), and when many
+  // blocks lie past their sequence's end, an order that leaves them out.
   const int g = id % Hkv;
-  const int rest = id / Hkv;
-  const int b = rest % p.n_seqs;
-  const int pblk = p.n_pblocks - 1 - rest / p.n_seqs;
-  const int s = p.cu[b];
-  const int L = p.cu[b + 1] - s;
+  const int item = id / Hkv;
+  int b = item % p.n_seqs;
+  int pblk = p.n_pblocks - 1 - item / p.n_seqs;
+  int s = p.cu[b];
+  int L = p.cu[b + 1] - s;
+  if (compact_grid(p.n_seqs, p.cu[p.n_seqs], p.max_seqlen)) {
+    int c0 = 0, c1 = 0;
+    if (lane_id() < p.n_seqs) {
+      c0 = p.cu[lane_id()];
+      c1 = p.cu[lane_id() + 1];
+    }
+    BlockItem bi;
+    const bool found = WINDOWED ? block_item_by_sequence(p.n_seqs, P, p.n_pblocks, item, c0, c1, bi)
+                                : block_item_by_level(p.n_seqs, P, p.n_pblocks, item, c0, c1, bi);
+    if (!found) return;
+    b = bi.seq;
+    pblk = bi.blk;
+    s = bi.start;
+    L = bi.len;
+  }
   const int p0 = pblk * P;
   if (p0 >= L) return;
   // With a KV cache the L new rows are the last L of the sequence's Lk cached
@@ -671,6 +688,7 @@ hipError_t launch_prefill_narrow(const PrefillArgs& a, int head_dim, hipStream_t
   kp.n_kv_heads = a.n_kv_heads;
   kp.n_seqs = a.n_seqs;
   kp.n_pblocks = (int32_t)pblocks128(a);
+  kp.max_seqlen = a.max_seqlen;
   kp.window = a.window > 0 ? a.window : 0;
   kp.c = (float)((double)a.softmax_scale * 1.4426950408889634);
   kp.seqlens_k = a.seqlens_k;

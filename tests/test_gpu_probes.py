@@ -178,10 +178,18 @@ def test_no_sequences_is_noop():
     assert torch.all(out == 3.0)
 
 
-def test_packed_equals_alone_bitwise():
-    wl = workloads.custom([70, 1, 300, 129, 0, 64], 16, 2, window=100, seed=6)
+@pytest.mark.parametrize("kernel", ["auto", "wide", "narrow"])
+@pytest.mark.parametrize("window", [0, 100])
+def test_packed_equals_alone_bitwise(window, kernel, monkeypatch):
+    """A sequence's rows do not depend on the sequences packed with it.  The ragged
+    pack has most of its grid's position blocks empty, so the kernels run it in their
+    compacted orders (by sequence with a window, by block index without); a sequence
+    alone fills its grid and takes the direct order."""
+    if kernel != "auto":
+        monkeypatch.setenv("TS_MHA_PREFILL_KERNEL", kernel)
+    wl = workloads.custom([70, 1, 300, 129, 0, 64, 1000], 16, 2, window=window, seed=6)
     inp = workloads.make_inputs(wl)
-    say("packed vs alone")
+    say(f"packed vs alone W={window} {kernel}")
     packed = run_gpu(inp).cpu()
     cu = inp["cu_seqlens"].tolist()
     for b in range(len(cu) - 1):
@@ -216,6 +224,17 @@ def test_wide_and_narrow_kernels_agree_bitwise(shape, qscale, monkeypatch):
     monkeypatch.setenv("TS_MHA_PREFILL_KERNEL", "narrow")
     b = run_gpu(inp).cpu()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("window", [0, 64])
+def test_many_sequences(window, oracle_lib):
+    """More sequences than the compacted orders serve (70 > 64, lengths 1 .. 300): the
+    direct order, empty blocks included, against the oracle."""
+    rng = np.random.default_rng(36)
+    wl = workloads.custom(rng.integers(1, 301, size=70).tolist(), 16, 2, window=window, seed=36)
+    inp = workloads.make_inputs(wl)
+    say(f"70 sequences W={window}")
+    assert_within_rounding(f64(run_gpu(inp).cpu()), inp, oracle_lib, what=f"70 sequences W={window}")
 
 
 def test_deterministic_bitwise():
