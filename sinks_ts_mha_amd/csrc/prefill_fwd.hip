@@ -170,22 +170,30 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   // overlap).
   int b = item % p.n_seqs;
   int pblk = p.n_pblocks - 1 - item / p.n_seqs;
-  int s = p.cu[b];
-  int L = p.cu[b + 1] - s;
-  if (compact_grid(p.n_seqs, p.cu[p.n_seqs], p.max_seqlen)) {
+  int s, L;
+  if (p.n_seqs <= kCompactMaxSeqs) {
+    // the sequence bounds, one per lane, in one load for either order
     int c0 = 0, c1 = 0;
     if (lane_id() < p.n_seqs) {
       c0 = p.cu[lane_id()];
       c1 = p.cu[lane_id() + 1];
     }
-    BlockItem bi;
-    const bool found = WINDOWED ? block_item_by_sequence(p.n_seqs, P, p.n_pblocks, item, c0, c1, bi)
-                                : block_item_by_level(p.n_seqs, P, p.n_pblocks, item, c0, c1, bi);
-    if (!found) return;
-    b = bi.seq;
-    pblk = bi.blk;
-    s = bi.start;
-    L = bi.len;
+    if (compact_grid(p.n_seqs, __builtin_amdgcn_readlane(c1, p.n_seqs - 1), p.max_seqlen)) {
+      BlockItem bi;
+      const bool found = WINDOWED ? block_item_by_sequence(p.n_seqs, P, p.n_pblocks, item, c0, c1, bi)
+                                  : block_item_by_level(p.n_seqs, P, p.n_pblocks, item, c0, c1, bi);
+      if (!found) return;
+      b = bi.seq;
+      pblk = bi.blk;
+      s = bi.start;
+      L = bi.len;
+    } else {
+      s = __builtin_amdgcn_readlane(c0, b);
+      L = __builtin_amdgcn_readlane(c1, b) - s;
+    }
+  } else {
+    s = p.cu[b];
+    L = p.cu[b + 1] - s;
   }
   const int p0 = pblk * P;
   if (p0 >= L) return;
