@@ -178,7 +178,8 @@ def cpu_baseline(wl, inp, target_s: float):
     stride = max(1, int(round(total_flops / max(rate * target_s, 1.0))))
     dt, flops, n = run(stride)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"every {stride}th packed token ({n} of {tok_all.size}), all {hq} q heads, "
+            "sample": (f"every packed token ({n})" if stride == 1 else
+                       f"one packed token in {stride} ({n} of {tok_all.size})") + f", all {hq} q heads, "
                       f"fp64 oracle rows; {dt:.1f} s wall"}
 
 
