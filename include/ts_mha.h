@@ -98,7 +98,8 @@ extern "C" {
  *               positions beyond it are not computed)
  *  stream       hipStream_t to enqueue on; NULL = the default stream
  *
- *  At head_dim 64 the call picks between two kernels with identical results:
+ *  At head_dim 64 the call picks between two kernels with bit-identical results
+ *  (the exact fallback included: both decide it per 128 query rows):
  *  work-groups of 256 query rows, or of 128 when the former would give no
  *  compute unit more than two work-groups (short or few sequences).  The
  *  environment variable TS_MHA_PREFILL_KERNEL=wide|narrow forces one of them

@@ -257,14 +257,20 @@ def test_window_covering_equals_full_bitwise():
         assert torch.equal(got.view(torch.int16), full.view(torch.int16)), f"W={w}"
 
 
-def test_output_fully_overwritten_and_guards_intact():
-    wl = workloads.custom([257, 3, 1024], 16, 2, window=0, seed=9)
+@pytest.mark.parametrize("kernel", ["wide", "narrow"])
+@pytest.mark.parametrize("window", [0, 100])
+def test_output_fully_overwritten_and_guards_intact(window, kernel, monkeypatch):
+    """Every output element is written and nothing outside the output is.  The ragged
+    pack leaves most of its grid's blocks empty, so this also checks that the compacted
+    orders give every block of every sequence to exactly one work-group."""
+    monkeypatch.setenv("TS_MHA_PREFILL_KERNEL", kernel)
+    wl = workloads.custom([257, 3, 1024, 0, 65], 16, 2, window=window, seed=9)
     inp = workloads.make_inputs(wl)
     n = inp["q"].numel()
     guard = 4096
     buf = torch.full((n + 2 * guard,), float("nan"), dtype=torch.bfloat16, device="cuda")
     out = buf[guard:guard + n].view(inp["q"].shape)
-    say("NaN-poisoned output with guard bands")
+    say(f"NaN-poisoned output with guard bands W={window} {kernel}")
     run_gpu(inp, out=out)
     torch.cuda.synchronize()
     assert not torch.isnan(out).any(), "some output element was not written"
