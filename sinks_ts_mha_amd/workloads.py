@@ -84,6 +84,11 @@ WORKLOADS = {
     "long_1x32768": Workload(
         "long_1x32768", (32768,), 64, 8,
         notes="1 sequence of 32768 tokens, 64 q / 8 KV heads, full causal, sinks"),
+    # One GPU's share when the layer's 8 KV-head groups are spread over 8 GPUs
+    # (no exchange needed): one KV head, its 8 query heads and their 8 sinks.
+    "gptoss_full_4x2048_kvgroup": Workload(
+        "gptoss_full_4x2048_kvgroup", (2048,) * 4, 8, 1,
+        notes="one KV-head group of the GPT-OSS full-causal layer: 4 x 2048 packed, 8 q / 1 KV head, sinks"),
 }
 
 # The other head width of the kernel traits the TokenSpeed-kernel README lists

@@ -66,7 +66,8 @@ def test_small_parity(case, kernel, oracle_lib, monkeypatch):
     assert_within_rounding(got, inp, oracle_lib, what=f"seqlens={seqlens} W={w}")
 
 
-FULL = ["tiny_1x128_gqa4", "gptoss_full_4x2048", "gptoss_window128_4x2048", "varlen16_window128"]
+FULL = ["tiny_1x128_gqa4", "gptoss_full_4x2048", "gptoss_window128_4x2048", "varlen16_window128",
+        "gptoss_full_4x2048_kvgroup"]
 
 
 @pytest.mark.parametrize("name", FULL)
