@@ -105,6 +105,37 @@ def test_long_prefill_sampled_rows(oracle_lib):
     assert excess.max() <= 0, f"rounding bound exceeded by {excess.max():.3e}"
 
 
+@pytest.mark.parametrize("window", [0, 128])
+@pytest.mark.parametrize("n_seqs", [64, 65])
+def test_ragged_pack_sampled_rows(n_seqs, window, oracle_lib):
+    """A large ragged pack at the GPT-OSS head shape: lengths uniform in [1, 3000] (seeded), so
+    about half of the grid's position blocks are empty.  With 64 sequences the launch runs
+    the compacted orders (by block level without a window, by sequence with one) over
+    thousands of work-groups; with 65 the direct order.  In every sequence the first 16
+    positions, the last 16 and every 509th, every query head, against the oracle's row
+    routine, under the gate and the rounding bound."""
+    rng = np.random.default_rng(37 + n_seqs)
+    lens = rng.integers(1, 3001, size=n_seqs).tolist()
+    wl = workloads.custom(lens, 64, 8, window=window, seed=37)
+    inp = workloads.make_inputs(wl)
+    say(f"ragged pack n_seqs={n_seqs} W={window} T={wl.total_tokens}")
+    out = run_gpu(inp).cpu()
+    cu = wl.cu_seqlens().tolist()
+    pos = []
+    for b in range(len(cu) - 1):
+        L = cu[b + 1] - cu[b]
+        rel = np.unique(np.concatenate([np.arange(min(16, L)), np.arange(max(0, L - 16), L), np.arange(0, L, 509)]))
+        pos.append(cu[b] + rel)
+    pos = np.concatenate(pos)
+    rows = np.repeat(pos, wl.n_q_heads)
+    heads = np.tile(np.arange(wl.n_q_heads), pos.size)
+    got = f64(out[torch.from_numpy(rows), torch.from_numpy(heads)])
+    ref = oracle.prefill_rows(*oracle_args(inp), rows=rows, heads=heads, lib=oracle_lib)
+    check(got, ref, f"ragged n_seqs={n_seqs} W={window}")
+    excess = np.abs(got - ref) - rounding_bound(inp, ref, oracle_lib, rows=rows, heads=heads)
+    assert excess.max() <= 0, f"rounding bound exceeded by {excess.max():.3e}"
+
+
 # 1x1K, 2x1K and 1x2K run the 128-row kernel (their 256-row grids would leave CU slots empty)
 SWEEP_CASES = ["sweep_b1_s1024", "sweep_b2_s1024", "sweep_b1_s2048", "sweep_b16_s1024",
                "sweep_b2_s4096", "sweep_b1_s8192", "sweep_b16_s8192"]
