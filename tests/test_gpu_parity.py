@@ -106,16 +106,17 @@ def test_long_prefill_sampled_rows(oracle_lib):
 
 
 @pytest.mark.parametrize("window", [0, 128])
-@pytest.mark.parametrize("n_seqs", [64, 65])
+@pytest.mark.parametrize("n_seqs", [64, 256, 257])
 def test_ragged_pack_sampled_rows(n_seqs, window, oracle_lib):
-    """A large ragged pack at the GPT-OSS head shape: lengths uniform in [1, 3000] (seeded), so
-    about half of the grid's position blocks are empty.  With 64 sequences the launch runs
-    the compacted orders (by block level without a window, by sequence with one) over
-    thousands of work-groups; with 65 the direct order.  In every sequence the first 16
-    positions, the last 16 and every 509th, every query head, against the oracle's row
-    routine, under the gate and the rounding bound."""
+    """A large ragged pack at the GPT-OSS head shape: lengths uniform in [1, m] (seeded;
+    m = 3000 for 64 sequences, 780 for more), so about half of the grid's position blocks
+    are empty.  With 64 sequences the launch runs the compacted orders (by block level
+    without a window, by sequence with one) over thousands of work-groups; with more, the
+    direct order.  In every sequence the first 16 positions, the last 16 and every 509th,
+    every query head, against the oracle's row routine, under the gate and the rounding
+    bound."""
     rng = np.random.default_rng(37 + n_seqs)
-    lens = rng.integers(1, 3001, size=n_seqs).tolist()
+    lens = rng.integers(1, (3001 if n_seqs <= 64 else 781), size=n_seqs).tolist()
     wl = workloads.custom(lens, 64, 8, window=window, seed=37)
     inp = workloads.make_inputs(wl)
     say(f"ragged pack n_seqs={n_seqs} W={window} T={wl.total_tokens}")

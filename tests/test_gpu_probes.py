@@ -227,14 +227,15 @@ def test_wide_and_narrow_kernels_agree_bitwise(shape, qscale, monkeypatch):
 
 
 @pytest.mark.parametrize("window", [0, 64])
-def test_many_sequences(window, oracle_lib):
-    """More sequences than the compacted orders serve (70 > 64, lengths 1 .. 300): the
-    direct order, empty blocks included, against the oracle."""
-    rng = np.random.default_rng(36)
-    wl = workloads.custom(rng.integers(1, 301, size=70).tolist(), 16, 2, window=window, seed=36)
+@pytest.mark.parametrize("n_seqs", [70, 256, 257])
+def test_many_sequences(n_seqs, window, oracle_lib):
+    """Many short sequences (lengths 1 .. 300), more than the compacted orders serve (64):
+    the direct order with its empty blocks, against the oracle."""
+    rng = np.random.default_rng(36 + n_seqs)
+    wl = workloads.custom(rng.integers(1, 301, size=n_seqs).tolist(), 16, 2, window=window, seed=36)
     inp = workloads.make_inputs(wl)
-    say(f"70 sequences W={window}")
-    assert_within_rounding(f64(run_gpu(inp).cpu()), inp, oracle_lib, what=f"70 sequences W={window}")
+    say(f"{n_seqs} sequences W={window}")
+    assert_within_rounding(f64(run_gpu(inp).cpu()), inp, oracle_lib, what=f"{n_seqs} sequences W={window}")
 
 
 def test_deterministic_bitwise():
