@@ -238,6 +238,22 @@ def test_many_sequences(n_seqs, window, oracle_lib):
     assert_within_rounding(f64(run_gpu(inp).cpu()), inp, oracle_lib, what=f"{n_seqs} sequences W={window}")
 
 
+@pytest.mark.parametrize("kernel", ["wide", "narrow"])
+@pytest.mark.parametrize("window", [0, 128])
+def test_max_seqlen_only_sizes_the_grid(window, kernel, monkeypatch):
+    """max_seqlen bounds the sequence lengths and sizes the grid, nothing more: a bound
+    4x too large (three quarters of the grid empty, so the compacted orders run) or
+    exactly 1 past the longest sequence gives the exact bound's output bit for bit."""
+    monkeypatch.setenv("TS_MHA_PREFILL_KERNEL", kernel)
+    wl = workloads.custom([512, 512, 300, 512], 64, 8, window=window, seed=38)
+    inp = workloads.make_inputs(wl)
+    say(f"max_seqlen padding W={window} {kernel}")
+    ref = run_gpu(inp).cpu()
+    for m in (513, 2048):
+        got = run_gpu(dict(inp, max_seqlen=m)).cpu()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"max_seqlen={m}"
+
+
 def test_deterministic_bitwise():
     wl = workloads.WORKLOADS["gptoss_full_4x2048"]
     inp = workloads.make_inputs(wl)
