@@ -35,6 +35,7 @@ struct DecodePlan {
   int32_t chunk;
   int32_t n_splits;
   int64_t workspace_bytes;
+  int32_t heads_per_group;    // KV heads per work-group (1, 2 or 4)
 };
 
 // The plan for these shapes, or n_splits = -1 if the launch would not fit.

@@ -11,14 +11,21 @@
 // and query head, so it is bound by HBM bandwidth, not by the matrix cores.
 // The design is about keeping enough bytes in flight:
 //
-// Work decomposition.  One work-group per (sequence, KV head, key chunk); the
-// host picks the chunk length (a multiple of 128 keys, at most 8192) so that
-// the grid fills every CU once (a work-group takes most of a CU's LDS), and
-// does not split a sequence when there are enough (sequence, KV head) pairs.  Its four waves take the chunk's
-// 32-key tiles round robin; each wave streams its tiles through a private
-// ring of four LDS stages with wave-wide buffer-to-LDS loads, three tiles
-// ahead, so the walk needs no barrier.  Every cached row is read once per
-// call, so the loads carry the non-temporal hint.
+// Work decomposition.  One work-group per (sequence, group of HW adjacent KV
+// heads, key chunk), HW in {1, 2, 4}; the host picks the chunk length (a
+// multiple of 128 keys, at most 8192) so that the grid fills every CU once (a
+// work-group takes most of a CU's LDS), and does not split a sequence when
+// there are enough (sequence, head group) pairs.  Wave w serves KV head
+// w % HW of the group and takes every (4 / HW)-th 32-key tile of the chunk;
+// each wave streams its tiles through a private ring of LDS stages with
+// wave-wide buffer-to-LDS loads, several tiles ahead, so the walk needs no
+// barrier.  A cached key's row holds all KV heads side by side, so with HW
+// heads per work-group the waves of one CU read HW * 2 * head_dim contiguous
+// bytes of each row at about the same time instead of one head's 2 * head_dim
+// bytes at a stride of the whole row: at head_dim 64 and 8 KV heads, 128-byte
+// pieces 1 KiB apart reach about 10% less of the HBM bandwidth than 512-byte
+// ones.  Every cached row is read once per call, so the loads carry the
+// non-temporal hint.
 //
 // Paging.  A 32-key tile is loaded as four groups of 8 keys; with pages of at
 // least 16 keys a group never straddles a page, so each load takes one page
@@ -35,7 +42,7 @@
 // except the tile maximum over the four lane groups.  Softmax in base 2:
 // t = s * scale * log2(e).
 //
-// Merge.  The four waves combine their (m, l, O) through LDS.  With one chunk
+// Merge.  The waves of each KV head combine their (m, l, O) through LDS.  With one chunk
 // per sequence the work-group adds the sink's term exp2(sigma - m), normalises
 // and stores bf16; otherwise it stores the chunk's (m, l, O) in fp32 and
 // decode_merge combines the chunks of each sequence and adds the sink.
@@ -44,6 +51,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "cdna4.h"
 
@@ -60,6 +68,8 @@ constexpr int kChunkMax = 8192;                   // keys per work-group at most
 constexpr int kMinPage = 16;
 constexpr int kPageSlots = kChunkMax / kMinPage + 2;
 constexpr int kTargetGroups = 256;                // one work-group per CU
+constexpr int kMaxGroupRowBytes = 512;            // a work-group's bytes of one cached row
+constexpr int kLongSpanTiles = 64;
 
 // Sizes that follow from head_dim D (64 or 128).
 template <int D>
@@ -129,9 +139,11 @@ __device__ __forceinline__ float lane_group_sum(float x) {
 
 }  // namespace
 
-template <int D, int G>
+template <int D, int G, int HW>
 __global__ void __launch_bounds__(kThreads, 1) decode_split(DParams p) {
   static_assert(G >= 1 && G <= 16, "the query heads of a KV head fill at most 16 MFMA columns");
+  static_assert(HW == 1 || HW == 2 || HW == 4, "KV heads per work-group");
+  constexpr int kWavesPerHead = kWaves / HW;  // waves that share one KV head's tiles
   using S = DShape<D>;
   constexpr int kD = D;
   constexpr int kRowBytes = S::kRowBytes;
@@ -147,13 +159,16 @@ __global__ void __launch_bounds__(kThreads, 1) decode_split(DParams p) {
   const int Hkv = p.n_kv_heads;
   const int Hq = Hkv * G;
   const int id = blockIdx.x;
-  const int g = id % Hkv;
-  const int rest = id / Hkv;
+  const int n_hg = Hkv / HW;
+  const int g0 = (id % n_hg) * HW;  // the work-group's first KV head
+  const int rest = id / n_hg;
   const int b = rest % p.n_seqs;
   const int split = rest / p.n_seqs;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const int g = g0 + w % HW;        // this wave's KV head
+  const int wr = w / HW;            // its rank among the waves of that head
   const int r16 = lane & 15;  // this lane's query (head g * G + r16 when r16 < G)
   const int grp = lane >> 4;
 
@@ -165,8 +180,9 @@ __global__ void __launch_bounds__(kThreads, 1) decode_split(DParams p) {
     // No key in this chunk.  With one chunk per sequence the rows are written
     // here (a sequence without keys has zero output); otherwise decode_merge
     // skips the chunk.
-    if (p.n_splits == 1 && tid < G * kD / 8)
-      *(u32x4*)(p.out + ((int64_t)b * Hq + g * G) * kD + tid * 8) = u32x4{0u, 0u, 0u, 0u};
+    if (p.n_splits == 1)
+      for (int i = tid; i < HW * G * kD / 8; i += kThreads)
+        *(u32x4*)(p.out + ((int64_t)b * Hq + g0 * G) * kD + i * 8) = u32x4{0u, 0u, 0u, 0u};
     return;
   }
 
@@ -192,8 +208,6 @@ __global__ void __launch_bounds__(kThreads, 1) decode_split(DParams p) {
 #pragma unroll
     for (int ks = 0; ks < S::kKS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
   }
-  float sink_t = -INFINITY;
-  if (p.sinks && r16 < G) sink_t = p.sinks[g * G + r16] * kLog2e;
   __syncthreads();  // page ids visible to every wave
   // The query loads complete here, before the tile loads below go out, so the
   // compiler's own waits never count those.
@@ -206,7 +220,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_split(DParams p) {
   // last tile still go out, with every lane out of range, so the number in
   // flight is the same on every iteration.
   const int nt = (end - start + kTileKeys - 1) / kTileKeys;
-  const int my_tiles = nt > w ? (nt - w + kWaves - 1) / kWaves : 0;
+  const int my_tiles = nt > wr ? (nt - wr + kWavesPerHead - 1) / kWavesPerHead : 0;
   const int pmask = (1 << p.page_shift) - 1;
   int dch[kLoads];
 #pragma unroll
@@ -216,7 +230,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_split(DParams p) {
   }
   const uint32_t ring_w = lds_addr(ring) + w * kWaveRing;
   auto issue = [&](int i) {
-    const int t = w + kWaves * i;
+    const int t = wr + kWavesPerHead * i;
     const bool live = i < my_tiles;
     const int tile_key = start + kTileKeys * t;
     const uint32_t dk = ring_w + (i % kStages) * 2 * kTileBytes;
@@ -264,7 +278,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_split(DParams p) {
     wait_vmem<(kStages - 1) * 2 * kLoads>();  // tile i has landed
     const lds_char* kt = (const lds_char*)ring + w * kWaveRing + (i % kStages) * 2 * kTileBytes;
     const lds_char* vt = kt + kTileBytes;
-    const int tile_key = start + kTileKeys * (w + kWaves * i);
+    const int tile_key = start + kTileKeys * (wr + kWavesPerHead * i);
     const bool edge = tile_key < lo || tile_key + kTileKeys > L;
 
     // S^T for keys 16 kb .. 16 kb + 15: element e is key 16 kb + 4 grp + e.
@@ -321,7 +335,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_split(DParams p) {
   // The loads past the last tile land before the wave may leave its LDS.
   wait_vmem<0>();
 
-  // ---- combine the four waves.  Each wave's O goes into its own part of the
+  // ---- combine the waves of each KV head.  Each wave's O goes into its own part of the
   // ring, which nothing reads or loads into any more: the wave's own reads of
   // it are done and its loads have landed.
   auto mo = [&](int v, int q, int d) -> float& {
@@ -339,24 +353,26 @@ __global__ void __launch_bounds__(kThreads, 1) decode_split(DParams p) {
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < G * kD / 4; idx += kThreads) {
-    const int q = idx / (kD / 4);
+  for (int idx = tid; idx < HW * G * kD / 4; idx += kThreads) {
+    const int hl = idx / (kD / 4);  // query head g0 * G + hl: KV head slot hl / G, query hl % G
+    const int q = hl % G;
+    const int w0 = hl / G;          // the waves of that KV head: w0, w0 + HW, ...
     const int d0 = 4 * (idx % (kD / 4));
-    const int h = g * G + q;
+    const int h = g0 * G + hl;
     float M = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, ml[v][q][0]);
+    for (int v = w0; v < kWaves; v += HW) M = fmaxf(M, ml[v][q][0]);
     float lt = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
+    for (int v = w0; v < kWaves; v += HW) {
       const float f = __builtin_amdgcn_exp2f(ml[v][q][0] - M);  // 0 for a wave without tiles
       lt = fmaf(f, ml[v][q][1], lt);
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[e] = fmaf(f, mo(v, q, d0 + e), acc[e]);
     }
     if (p.n_splits == 1) {
-      const float st = __shfl(sink_t, q);  // lane q holds the sink of query q (wave 0)
+      const float st = p.sinks ? p.sinks[h] * kLog2e : -INFINITY;
       float den = lt;
       float scale = 1.f;
       if (p.sinks) {
@@ -380,14 +396,22 @@ __global__ void __launch_bounds__(kThreads, 1) decode_split(DParams p) {
   }
 }
 
-// Combine the chunks of each (sequence, query head).  One work-group of
-// 16 x D / 4 threads per (sequence, query head): thread (sl, dc) folds chunks
-// sl, sl + 16, ... of head_dim elements 4 dc .. 4 dc + 3 into a running
-// (m, l, O), the 16 chunk
-// lanes then combine by a butterfly, and the sink's term joins the
-// denominator.  The chunk loads of one thread are independent, so the loop
-// keeps several in flight.
-constexpr int kMergeLanes = 16;
+// Combine the chunks of each (sequence, query head).  S x D / 4 threads per
+// (sequence, query head), S a power of two that the host picks from the number
+// of chunks (so that few chunks do not leave most threads idle, and many are
+// folded by many lanes): thread (sl, dc) folds chunks sl, sl + S, ... of
+// head_dim elements 4 dc .. 4 dc + 3 into a running (m, l, O), the S chunk
+// lanes (adjacent lanes of one wave) then combine by a butterfly, and the
+// sink's term joins the denominator.  A work-group takes 256 threads' worth of
+// rows, or one row when a row needs more.
+template <int D, int S>
+struct MergeShape {
+  static_assert(S >= 2 && S <= 16 && (S & (S - 1)) == 0, "chunk lanes");
+  static constexpr int kRowThreads = S * D / 4;
+  static_assert(kRowThreads <= 1024, "one row per work-group at most");
+  static constexpr int kRows = kRowThreads >= 256 ? 1 : 256 / kRowThreads;  // rows per work-group
+  static constexpr int kThreads = kRows * kRowThreads;
+};
 
 __device__ __forceinline__ void fold(float& m, float& l, f32x4& o, float m2, float l2, const f32x4& o2) {
   const float mn = fmaxf(m, m2);
@@ -400,26 +424,29 @@ __device__ __forceinline__ void fold(float& m, float& l, f32x4& o, float m2, flo
   m = mn;
 }
 
-template <int D>
-__global__ void __launch_bounds__(16 * D / 4) decode_merge(DParams p, int G) {
+template <int D, int S>
+__global__ void __launch_bounds__((MergeShape<D, S>::kThreads)) decode_merge(DParams p, int G) {
+  using M = MergeShape<D, S>;
   constexpr int kD = D;
   const int Hq = p.n_kv_heads * G;
-  const int h = blockIdx.x % Hq;
-  const int b = blockIdx.x / Hq;
-  const int tid = threadIdx.x;
-  const int sl = tid & (kMergeLanes - 1);
-  const int dc = tid >> 4;
+  const int bh = (int)blockIdx.x * M::kRows + (int)threadIdx.x / M::kRowThreads;  // b * Hq + h
+  if ((int64_t)bh >= (int64_t)p.n_seqs * Hq) return;  // every thread of a row returns together
+  const int h = bh % Hq;
+  const int b = bh / Hq;
+  const int tid = (int)threadIdx.x % M::kRowThreads;
+  const int sl = tid & (S - 1);
+  const int dc = tid / S;
   const int L = p.seqlens_k[b];
   const int n_valid = L > 0 ? min(p.n_splits, (L - first_tile_key(L, p.window) + p.chunk - 1) / p.chunk) : 0;
   float m = -INFINITY, l = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-  for (int s = sl; s < n_valid; s += kMergeLanes) {
+  for (int s = sl; s < n_valid; s += S) {
     const int64_t row = ((int64_t)s * p.n_seqs + b) * Hq + h;
     fold(m, l, o, p.ws_ml[2 * row], p.ws_ml[2 * row + 1], *(const f32x4*)(p.ws_o + row * kD + 4 * dc));
   }
 #pragma unroll
-  for (int x = 1; x < kMergeLanes; x <<= 1) {
+  for (int x = 1; x < S; x <<= 1) {
     f32x4 o2;
 #pragma unroll
     for (int e = 0; e < 4; ++e) o2[e] = __shfl_xor(o[e], x);
@@ -439,23 +466,40 @@ __global__ void __launch_bounds__(16 * D / 4) decode_merge(DParams p, int G) {
 namespace {
 
 template <int D, int G>
-hipError_t launch_group(const DParams& kp, int64_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split<D, G>), dim3((unsigned)grid), dim3(kThreads), 0, stream, kp);
+hipError_t launch_group(const DParams& kp, int64_t grid, int hw, hipStream_t stream) {
+  switch (hw) {
+    case 1: hipLaunchKernelGGL((decode_split<D, G, 1>), dim3((unsigned)grid), dim3(kThreads), 0, stream, kp); break;
+    case 2: hipLaunchKernelGGL((decode_split<D, G, 2>), dim3((unsigned)grid), dim3(kThreads), 0, stream, kp); break;
+    case 4: hipLaunchKernelGGL((decode_split<D, G, 4>), dim3((unsigned)grid), dim3(kThreads), 0, stream, kp); break;
+    default: return hipErrorInvalidValue;
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || kp.n_splits == 1) return err;
-  hipLaunchKernelGGL(decode_merge<D>, dim3((unsigned)(kp.n_seqs * kp.n_kv_heads * G)), dim3(16 * D / 4), 0,
-                     stream, kp, G);
+  const int64_t rows = (int64_t)kp.n_seqs * kp.n_kv_heads * G;
+  auto merge = [&](auto lanes) {
+    using M = MergeShape<D, decltype(lanes)::value>;
+    hipLaunchKernelGGL((decode_merge<D, decltype(lanes)::value>), dim3((unsigned)((rows + M::kRows - 1) / M::kRows)),
+                       dim3(M::kThreads), 0, stream, kp, G);
+  };
+  // chunk lanes: the chunks' count rounded up to a power of two, at most 16
+  // (more lanes lengthen the butterfly by more than they shorten the folds:
+  // 128 chunks of one sequence merge 5% slower with 64 lanes than with 16)
+  const int n = kp.n_splits;
+  if (n <= 2) merge(std::integral_constant<int, 2>{});
+  else if (n <= 4) merge(std::integral_constant<int, 4>{});
+  else if (n <= 8) merge(std::integral_constant<int, 8>{});
+  else merge(std::integral_constant<int, 16>{});
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(const DParams& kp, int64_t grid, int G, hipStream_t stream) {
+hipError_t launch_d(const DParams& kp, int64_t grid, int G, int hw, hipStream_t stream) {
   switch (G) {
-    case 1: return launch_group<D, 1>(kp, grid, stream);
-    case 2: return launch_group<D, 2>(kp, grid, stream);
-    case 4: return launch_group<D, 4>(kp, grid, stream);
-    case 8: return launch_group<D, 8>(kp, grid, stream);
-    case 16: return launch_group<D, 16>(kp, grid, stream);
+    case 1: return launch_group<D, 1>(kp, grid, hw, stream);
+    case 2: return launch_group<D, 2>(kp, grid, hw, stream);
+    case 4: return launch_group<D, 4>(kp, grid, hw, stream);
+    case 8: return launch_group<D, 8>(kp, grid, hw, stream);
+    case 16: return launch_group<D, 16>(kp, grid, hw, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -465,11 +509,24 @@ int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 }  // namespace
 
 DecodePlan decode_plan(const DecodeArgs& a) {
-  DecodePlan pl{0, -1, 0};
+  DecodePlan pl{0, -1, 0, 1};
   int64_t span = a.max_seqlen_k;
   if (a.window > 0) span = std::min<int64_t>(span, (int64_t)a.window + kTileKeys - 1);
   const int64_t tiles = std::max<int64_t>(1, (span + kTileKeys - 1) / kTileKeys);
-  const int64_t base = std::max<int64_t>(1, (int64_t)a.n_seqs * a.n_kv_heads);
+  // KV heads per work-group: the most (up to 512 contiguous bytes of a cached
+  // row) that still fill the grid without splitting the sequences, or, for
+  // spans of at least kLongSpanTiles tiles, whose split costs little against
+  // the walk, the most regardless.
+  int hw = 1;
+  for (int c = 4; c >= 2; c >>= 1) {
+    if (a.n_kv_heads % c != 0 || c * 2 * a.head_dim > kMaxGroupRowBytes) continue;
+    if ((int64_t)a.n_seqs * (a.n_kv_heads / c) >= kTargetGroups || tiles >= kLongSpanTiles) {
+      hw = c;
+      break;
+    }
+  }
+  pl.heads_per_group = hw;
+  const int64_t base = std::max<int64_t>(1, (int64_t)a.n_seqs * (a.n_kv_heads / hw));
   const int64_t want = std::max<int64_t>(1, (kTargetGroups + base - 1) / base);
   int64_t ct = (tiles + want - 1) / want;
   ct = std::min<int64_t>(std::max<int64_t>(4, (ct + 3) / 4 * 4), kChunkMax / kTileKeys);
@@ -511,9 +568,10 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, void* work
   kp.chunk = plan.chunk;
   kp.n_splits = plan.n_splits;
   kp.c = a.softmax_scale * kLog2e;
-  const int64_t grid = (int64_t)a.n_seqs * a.n_kv_heads * plan.n_splits;
-  if (a.head_dim == 128) return launch_d<128>(kp, grid, G, stream);
-  if (a.head_dim == 64) return launch_d<64>(kp, grid, G, stream);
+  const int hw = plan.heads_per_group;
+  const int64_t grid = (int64_t)a.n_seqs * (a.n_kv_heads / hw) * plan.n_splits;
+  if (a.head_dim == 128) return launch_d<128>(kp, grid, G, hw, stream);
+  if (a.head_dim == 64) return launch_d<64>(kp, grid, G, hw, stream);
   return hipErrorInvalidValue;
 }
 

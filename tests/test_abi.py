@@ -180,9 +180,10 @@ def test_decode_workspace_size():
     assert big > 0 and big % 4 == 0
     assert ws(1, 64, 8, 64, 0, 65536) == big  # a function of its arguments only
     assert ws(0, 64, 8, 64, 0, 0) == 0
-    # head_dim 128: the same split, twice the partial output per row
-    d128 = ws(1, 64, 8, 128, 0, 65536)
-    assert d128 > big and (d128 - big) % (64 * 4) == 0
+    # head_dim 128 with 2 KV heads (the same work-groups and split as head_dim 64): twice the
+    # partial output per row
+    d64, d128 = ws(1, 16, 2, 64, 0, 65536), ws(1, 16, 2, 128, 0, 65536)
+    assert d64 > 0 and d128 > d64 and (d128 - d64) % (16 * 64 * 4) == 0
     with pytest.raises(tm.TsMhaError):
         ws(1, 64, 8, 96, 0, 1024)
     with pytest.raises(tm.TsMhaError):

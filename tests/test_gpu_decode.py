@@ -178,3 +178,44 @@ def test_decode_graph_replay_matches_eager():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+
+
+HEAD_GROUP_CASES = [
+    # (k_lens rng spec (n_seqs, max len, share empty), Hq, Hkv, head_dim, window): the KV heads
+    # per work-group and whether sequences are split follow from the shapes
+    ((256, 300, 0.1), 16, 4, 64, 0),      # 4 heads per work-group, 256 work-groups, no split
+    ((128, 300, 0.1), 16, 4, 64, 33),     # 2 heads per work-group (4 would leave CUs idle)
+    ((86, 200, 0.1), 12, 6, 64, 0),       # 6 KV heads: 2 per work-group
+    ((256, 150, 0.2), 32, 2, 128, 0),     # head_dim 128, G = 16: 2 heads, 512 output chunks
+    ((256, 150, 0.2), 16, 2, 128, 100),
+    ((4, 9000, 0.25), 32, 4, 64, 2500),   # long windowed spans: 4 heads and split chunks
+    ((3, 6000, 0.0), 8, 8, 128, 0),       # head_dim 128, G = 1: 2 heads and split chunks
+]
+
+
+@pytest.mark.parametrize("case", HEAD_GROUP_CASES, ids=[f"hg{n}" for n in range(len(HEAD_GROUP_CASES))])
+def test_decode_head_groups(case, oracle_lib):
+    """Work-groups that serve several adjacent KV heads (their waves split between the heads),
+    with and without split sequences: against the oracle under the gate and the rounding
+    bound, empty sequences give zero rows, and nothing outside the output is written."""
+    (n, max_len, p_empty), hq, hkv, d, w = case
+    rng = np.random.default_rng(71 + n + d + w)
+    k_lens = rng.integers(1, max_len + 1, size=n)
+    k_lens[rng.random(n) < p_empty] = 0
+    k_lens = k_lens.tolist()
+    wl = workloads.decode(k_lens, n_q_heads=hq, n_kv_heads=hkv, window=w, page_size=16, seed=72,
+                          head_dim=d, softmax_scale=d ** -0.5)
+    inp = workloads.make_cache_inputs(wl)
+    inp["sinks"] = inp["sinks"] * 2.0
+    say(f"decode head groups n_seqs={n} Hq={hq} Hkv={hkv} D={d} W={w}")
+    dev = torch.device("cuda", 0)
+    guard = torch.full((inp["q"].numel() + 2 * 4096,), float("nan"), dtype=torch.bfloat16, device=dev)
+    out = guard[4096:4096 + inp["q"].numel()].view(inp["q"].shape)
+    run_gpu_decode(inp, out=out)
+    torch.cuda.synchronize()
+    assert torch.isnan(guard[:4096]).all() and torch.isnan(guard[-4096:]).all()
+    got = f64(out.cpu())
+    ref = oracle.cache_attend(*cache_oracle_args(inp), lib=oracle_lib)
+    check(got, ref, f"n_seqs={n} G={hq // hkv} D={d} W={w}", bound=cache_rounding_bound(inp, ref, oracle_lib))
+    empty = [b for b, L in enumerate(k_lens) if L == 0]
+    assert np.all(got[empty] == 0.0), "a sequence without keys must give zero rows"
