@@ -71,6 +71,7 @@
 
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "cdna4.h"
@@ -93,6 +94,7 @@ constexpr int kTileChunks = kBK * kChunks;    // 16-byte chunks per tile
 constexpr int kTileBytes = kTileChunks * 16;
 constexpr int kFastSumBinades = 64;  // the fast pass keeps row sums in [2^-64, 2^65)
 constexpr int kSlots = 2;                     // LDS buffers for K and for V tiles
+constexpr int64_t kSeqGroupBytes = 4 << 20;   // one XCD's L2
 constexpr int kMaskCausal = 1;                // mask kinds: key past the row's position
 constexpr int kMaskWindow = 2;                // ... key before the row's window
 
@@ -118,6 +120,7 @@ struct KParams {
   int32_t pages_per_seq;
   int32_t n_pages;
   int32_t max_seqlen;
+  int32_t seq_group;  // sequences per group of the direct order (>= 1)
 };
 
 namespace {
@@ -168,8 +171,21 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   // return at once; a windowed layer's blocks all carry about the same work,
   // so its order only keeps a sequence's blocks together (their K/V tiles
   // overlap).
-  int b = item % p.n_seqs;
-  int pblk = p.n_pblocks - 1 - item / p.n_seqs;
+  //
+  // The direct order takes the sequences in groups of p.seq_group, whose K and
+  // V fit one XCD's L2 (all sequences when they fit together), and runs the
+  // blocks of one group last-first before the next group's: the work-groups in
+  // flight then share their K/V tiles in L2 instead of sweeping the K/V of
+  // every sequence of a large batch through it.
+  int b, pblk;
+  {
+    const int per_group = p.seq_group * p.n_pblocks;
+    const int grp = item / per_group;
+    const int r = item - grp * per_group;
+    const int gs = min(p.seq_group, p.n_seqs - grp * p.seq_group);  // the last group may hold fewer
+    b = grp * p.seq_group + r % gs;
+    pblk = p.n_pblocks - 1 - r / gs;
+  }
   int s, L;
   if (p.n_seqs <= kCompactMaxSeqs) {
     // the sequence bounds, one per lane, in one load for either order
@@ -797,6 +813,13 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   kp.pages_per_seq = a.pages_per_seq;
   kp.n_pages = a.n_pages;
   kp.max_seqlen = a.max_seqlen;
+  {
+    // K and V of one sequence as one XCD's L2 sees them (the KV heads that
+    // land on one XCD: one when there are 8 or fewer)
+    const int64_t per_seq =
+        std::max<int64_t>(1, (int64_t)a.max_seqlen * 2 * kRowBytes * std::max(1, a.n_kv_heads / 8));
+    kp.seq_group = (int32_t)std::min<int64_t>(std::max<int64_t>(kSeqGroupBytes / per_seq, 1), std::max(1, a.n_seqs));
+  }
   const bool windowed = a.window > 0;
   const bool paged = a.block_table != nullptr;
   (void)hipGetLastError();  // start from a clean per-thread error state

@@ -202,6 +202,34 @@ def test_packed_equals_alone_bitwise(window, kernel, monkeypatch):
         assert torch.equal(alone.view(torch.int16), packed[s:e].view(torch.int16)), f"sequence {b}"
 
 
+@pytest.mark.parametrize("shape,check", [
+    (([8192] * 3, 0), None),               # groups of 2 sequences: {0, 1}, {2}
+    (([4096] * 5 + [4000], 128), None),    # groups of 4: {0..3}, {4, 5}
+    (([1024] * 70, 0), [0, 15, 16, 31, 47, 63, 64, 69]),  # groups of 16, the last of 6
+], ids=["3x8192", "6x4096_w128", "70x1024"])
+def test_sequence_groups_packed_equals_alone(shape, check):
+    """Uniform batches run in the direct order, which takes the sequences in groups whose
+    K and V fit one XCD's L2 (4 MiB: 2 sequences of 8192 tokens, 4 of 4096, 16 of 1024 at
+    8 KV heads), the last group smaller.  Every row of the batch, written over NaN, equals
+    its sequence run alone bit for bit (a block left out or run twice or at the wrong
+    sequence would differ)."""
+    (seqlens, w) = shape
+    wl = workloads.custom(seqlens, 64, 8, window=w, seed=21)
+    inp = workloads.make_inputs(wl)
+    say(f"sequence groups {len(seqlens)} x {max(seqlens)} W={w}")
+    dev = torch.device("cuda", 0)
+    out = torch.full(inp["q"].shape, float("nan"), dtype=torch.bfloat16, device=dev)
+    packed = run_gpu(inp, out=out).cpu()
+    cu = inp["cu_seqlens"].tolist()
+    for b in (range(len(seqlens)) if check is None else check):
+        s, e = cu[b], cu[b + 1]
+        one = dict(inp, q=inp["q"][s:e], k=inp["k"][s:e], v=inp["v"][s:e],
+                   cu_seqlens=torch.tensor([0, e - s], dtype=torch.int32), max_seqlen=e - s)
+        alone = run_gpu(one).cpu()
+        assert torch.equal(alone.view(torch.int16), packed[s:e].view(torch.int16)), f"sequence {b}"
+    assert not torch.isnan(packed).any()
+
+
 @pytest.mark.parametrize("qscale", [1.0, 40.0], ids=["fast", "redo"])
 @pytest.mark.parametrize("shape", [([70, 1, 300, 129, 0, 64], 16, 2, 100), ([1000, 333], 64, 8, 0),
                                    ([2048] * 2, 64, 8, 128), ([517, 65, 1], 32, 2, 0), ([300], 8, 8, 0)],
