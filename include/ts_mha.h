@@ -226,6 +226,11 @@ int ts_mha_prefill_with_kvcache(const void* q, const void* k_cache, const void* 
  *  read outside the block table or the cache pool (page ids are clamped into
  *  the pool), but the results are then meaningless; TS_MHA_VALIDATE=1 checks
  *  them on the host first (a synchronising read-back).
+ *  How the keys are divided among work-groups (how many adjacent KV heads one
+ *  work-group serves, and the split of long sequences into key chunks) follows
+ *  from n_seqs, n_q_heads, n_kv_heads, head_dim, window and max_seqlen_k only:
+ *  calls with equal values give identical bits, and a row's last bits may
+ *  differ between calls with different ones (another summation order).
  *  Returns TS_MHA_OK or a TS_MHA_ERR_* code.
  */
 int ts_mha_decode_with_kvcache(const void* q, const void* k_cache, const void* v_cache,
