@@ -204,6 +204,24 @@ __device__ __forceinline__ bool compact_grid(int n_seqs, int total_rows, int max
   return n_seqs <= kCompactMaxSeqs && 5LL * total_rows < 4LL * n_seqs * max_seqlen;
 }
 
+// Direct order of the position blocks of n_seqs sequences (n_levels blocks
+// each): the sequences in groups of `group` (the last group may hold fewer),
+// one group's blocks before the next group's, and within a group block level
+// last-first, by sequence within a level.  Under a causal mask the late blocks
+// carry the most key tiles, so the longest work of a group starts first; a
+// group small enough that its K and V fit one XCD's L2 keeps the K/V tiles
+// that the work-groups in flight read there, instead of sweeping every
+// sequence's K/V of a large batch through it.
+__device__ __forceinline__ void direct_block_item(int item, int n_seqs, int n_levels, int group, int& seq,
+                                                  int& blk) {
+  const int per_group = group * n_levels;
+  const int grp = item / per_group;
+  const int r = item - grp * per_group;
+  const int gs = min(group, n_seqs - grp * group);
+  seq = grp * group + r % gs;
+  blk = n_levels - 1 - r / gs;
+}
+
 // Position of 16-byte chunk `ch` of row `row` (8 chunks of a 128-byte row) in
 // an LDS tile.  The LDS serves 64 banks of 4 bytes per cycle, two 128-byte
 // rows; the XOR key (row bit 1 as chunk bit 2, row bits 2..3 as chunk bits

@@ -36,6 +36,11 @@ int64_t prefill_grid_size(const PrefillArgs& a);
 // Enqueue the kernel; returns the launch's hipError_t.
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
+// Sequences per group of the kernels' direct order (cdna4.h, direct_block_item):
+// as many as have their K and V (rows of row_bytes per KV head) within one
+// XCD's L2, at least 1, at most n_seqs.
+int32_t prefill_seq_group(const PrefillArgs& a, int row_bytes);
+
 // The same two calls for the 128-row work-groups of prefill_fwd_narrow.hip, at
 // head_dim 64 or 128 (a paged cache at head_dim 128 only: the grid size is -1
 // for a paged cache at head_dim 64).

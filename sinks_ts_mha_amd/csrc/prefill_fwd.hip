@@ -165,27 +165,15 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fwd_d64(KParams p) {
   const int g = id % Hkv;
   const int item = id / Hkv;
   // Position blocks are issued last-first: under a causal mask the late blocks
-  // carry the most key tiles, so the longest work starts first.  When many
+  // carry the most key tiles, so the longest work starts first (in groups of
+  // sequences whose K/V fit one XCD's L2, cdna4.h's direct order).  When many
   // blocks lie past their sequence's end (the grid is sized for the longest
   // sequence) the order leaves them out, and its surplus ids come last and
   // return at once; a windowed layer's blocks all carry about the same work,
   // so its order only keeps a sequence's blocks together (their K/V tiles
   // overlap).
-  //
-  // The direct order takes the sequences in groups of p.seq_group, whose K and
-  // V fit one XCD's L2 (all sequences when they fit together), and runs the
-  // blocks of one group last-first before the next group's: the work-groups in
-  // flight then share their K/V tiles in L2 instead of sweeping the K/V of
-  // every sequence of a large batch through it.
   int b, pblk;
-  {
-    const int per_group = p.seq_group * p.n_pblocks;
-    const int grp = item / per_group;
-    const int r = item - grp * per_group;
-    const int gs = min(p.seq_group, p.n_seqs - grp * p.seq_group);  // the last group may hold fewer
-    b = grp * p.seq_group + r % gs;
-    pblk = p.n_pblocks - 1 - r / gs;
-  }
+  direct_block_item(item, p.n_seqs, p.n_pblocks, p.seq_group, b, pblk);
   int s, L;
   if (p.n_seqs <= kCompactMaxSeqs) {
     // the sequence bounds, one per lane, in one load for either order
@@ -779,6 +767,14 @@ int64_t pblocks(const PrefillArgs& a) {
 
 }  // namespace
 
+int32_t prefill_seq_group(const PrefillArgs& a, int row_bytes) {
+  // K and V of one sequence as one XCD's L2 sees them: consecutive work-group
+  // ids go to different XCDs with the KV head fastest, so one XCD serves
+  // n_kv_heads / 8 KV heads (one when there are 8 or fewer)
+  const int64_t per_seq = std::max<int64_t>(1, (int64_t)a.max_seqlen * 2 * row_bytes * std::max(1, a.n_kv_heads / 8));
+  return (int32_t)std::min<int64_t>(std::max<int64_t>(kSeqGroupBytes / per_seq, 1), std::max(1, a.n_seqs));
+}
+
 int64_t prefill_grid_size(const PrefillArgs& a) {
   // each sequence's K (or V) rows must be addressable by one buffer descriptor
   // (a cache is addressed page by page instead)
@@ -813,13 +809,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   kp.pages_per_seq = a.pages_per_seq;
   kp.n_pages = a.n_pages;
   kp.max_seqlen = a.max_seqlen;
-  {
-    // K and V of one sequence as one XCD's L2 sees them (the KV heads that
-    // land on one XCD: one when there are 8 or fewer)
-    const int64_t per_seq =
-        std::max<int64_t>(1, (int64_t)a.max_seqlen * 2 * kRowBytes * std::max(1, a.n_kv_heads / 8));
-    kp.seq_group = (int32_t)std::min<int64_t>(std::max<int64_t>(kSeqGroupBytes / per_seq, 1), std::max(1, a.n_seqs));
-  }
+  kp.seq_group = prefill_seq_group(a, kRowBytes);
   const bool windowed = a.window > 0;
   const bool paged = a.block_table != nullptr;
   (void)hipGetLastError();  // start from a clean per-thread error state

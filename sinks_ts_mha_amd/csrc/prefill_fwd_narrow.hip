@@ -92,6 +92,7 @@ struct Params {
   int32_t n_seqs;
   int32_t n_pblocks;
   int32_t max_seqlen;
+  int32_t seq_group;  // sequences per group of the direct order (>= 1)
   int32_t window;
   float c;  // softmax_scale * log2(e)
   // paged K/V only: k and v are the caches [n_pages][page_size][n_kv_heads][D]
@@ -151,12 +152,13 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 3 : 2) prefill_fwd_narrow(
   const int Hq = Hkv * G;
   const int id = blockIdx.x;
   // KV head fastest (each XCD's L2 serves a fixed set of heads), position
-  // blocks last-first (the longest causal work starts first), and when many
-  // blocks lie past their sequence's end, an order that leaves them out.
+  // blocks last-first (the longest causal work starts first) in groups of
+  // sequences whose K/V fit one XCD's L2, and when many blocks lie past their
+  // sequence's end, an order that leaves them out.
   const int g = id % Hkv;
   const int item = id / Hkv;
-  int b = item % p.n_seqs;
-  int pblk = p.n_pblocks - 1 - item / p.n_seqs;
+  int b, pblk;
+  direct_block_item(item, p.n_seqs, p.n_pblocks, p.seq_group, b, pblk);
   int s, L;
   if (p.n_seqs <= kCompactMaxSeqs) {
     // the sequence bounds, one per lane, in one load for either order
@@ -697,6 +699,7 @@ hipError_t launch_prefill_narrow(const PrefillArgs& a, int head_dim, hipStream_t
   kp.n_seqs = a.n_seqs;
   kp.n_pblocks = (int32_t)pblocks128(a);
   kp.max_seqlen = a.max_seqlen;
+  kp.seq_group = prefill_seq_group(a, 2 * head_dim);
   kp.window = a.window > 0 ? a.window : 0;
   kp.c = (float)((double)a.softmax_scale * 1.4426950408889634);
   kp.seqlens_k = a.seqlens_k;
