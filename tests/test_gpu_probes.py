@@ -203,20 +203,22 @@ def test_packed_equals_alone_bitwise(window, kernel, monkeypatch):
 
 
 @pytest.mark.parametrize("shape,check", [
-    (([8192] * 3, 0), None),               # groups of 2 sequences: {0, 1}, {2}
-    (([4096] * 5 + [4000], 128), None),    # groups of 4: {0..3}, {4, 5}
-    (([1024] * 70, 0), [0, 15, 16, 31, 47, 63, 64, 69]),  # groups of 16, the last of 6
-], ids=["3x8192", "6x4096_w128", "70x1024"])
+    (([8192] * 3, 0, 64), None),               # groups of 2 sequences: {0, 1}, {2}
+    (([4096] * 5 + [4000], 128, 64), None),    # groups of 4: {0..3}, {4, 5}
+    (([1024] * 70, 0, 64), [0, 15, 16, 31, 47, 63, 64, 69]),  # groups of 16, the last of 6
+    (([4096] * 5, 0, 128), None),              # head_dim 128, groups of 2: {0, 1}, {2, 3}, {4}
+    (([2048] * 9, 100, 128), [0, 3, 4, 7, 8]),  # head_dim 128, groups of 4, the last of 1
+], ids=["3x8192", "6x4096_w128", "70x1024", "d128_5x4096", "d128_9x2048_w100"])
 def test_sequence_groups_packed_equals_alone(shape, check):
     """Uniform batches run in the direct order, which takes the sequences in groups whose
-    K and V fit one XCD's L2 (4 MiB: 2 sequences of 8192 tokens, 4 of 4096, 16 of 1024 at
-    8 KV heads), the last group smaller.  Every row of the batch, written over NaN, equals
-    its sequence run alone bit for bit (a block left out or run twice or at the wrong
-    sequence would differ)."""
-    (seqlens, w) = shape
-    wl = workloads.custom(seqlens, 64, 8, window=w, seed=21)
+    K and V fit one XCD's L2 (4 MiB: at 8 KV heads and head_dim 64, 2 sequences of 8192
+    tokens, 4 of 4096, 16 of 1024; half as many at head_dim 128), the last group smaller.
+    Every row of the batch, written over NaN, equals its sequence run alone bit for bit (a
+    block left out or run twice or at the wrong sequence would differ)."""
+    (seqlens, w, d) = shape
+    wl = workloads.custom(seqlens, 64, 8, window=w, head_dim=d, softmax_scale=d ** -0.5, seed=21)
     inp = workloads.make_inputs(wl)
-    say(f"sequence groups {len(seqlens)} x {max(seqlens)} W={w}")
+    say(f"sequence groups {len(seqlens)} x {max(seqlens)} W={w} D={d}")
     dev = torch.device("cuda", 0)
     out = torch.full(inp["q"].shape, float("nan"), dtype=torch.bfloat16, device=dev)
     packed = run_gpu(inp, out=out).cpu()
