@@ -65,6 +65,8 @@ def call(q=FAKE, k=FAKE, v=FAKE, sinks=None, cu=FAKE, hq=64, hkv=8, d=64, window
     (dict(max_seqlen=2**21, hq=8, hkv=8, n_seqs=1), -2),
     # at head_dim 128: (131100 + 128) * 64 heads * 256 B
     (dict(d=128, max_seqlen=131100, n_seqs=1), -2),
+    # one token past the largest accepted sequence (see test_validation_precedes_device_check)
+    (dict(max_seqlen=261888, n_seqs=1), -2), (dict(d=128, max_seqlen=130944, n_seqs=1), -2),
     (dict(d=256), -3), (dict(d=96), -3), (dict(d=32), -3), (dict(hq=24, hkv=8), -3),
     (dict(hq=64, hkv=2), -3), (dict(d=128, hq=64, hkv=2), -3),
     (dict(scale=0.0), -4), (dict(scale=-0.1), -4), (dict(scale=float("nan")), -4),
@@ -85,6 +87,9 @@ def test_validation_precedes_device_check():
     assert call(window=128, sinks=FAKE) == -6
     assert call(n_seqs=0, max_seqlen=0) == -6
     assert call(max_seqlen=261000, n_seqs=1) == -6  # just inside the q-row limit
+    # the largest accepted sequences: (L + 256) * 64 heads * 128 B and (L + 128) * 64 * 256 B
+    # within 2^31 - 1 (the GPU parity suite runs both)
+    assert call(max_seqlen=261887, n_seqs=1) == -6 and call(d=128, max_seqlen=130943, n_seqs=1) == -6
     assert call(d=128) == -6 and call(d=128, window=128, sinks=FAKE) == -6
     assert call(d=128, max_seqlen=130000, n_seqs=1) == -6  # inside the head_dim 128 limit
 

@@ -165,3 +165,35 @@ def test_chart_point_sampled_rows(name, oracle_lib):
     check(got[rows, heads], ref, f"{name} sampled")
     excess = np.abs(got[rows, heads] - ref) - rounding_bound(inp, ref, oracle_lib, rows=rows, heads=heads)
     assert excess.max() <= 0, f"{name}: rounding bound exceeded by {excess.max():.3e}"
+
+
+@pytest.mark.parametrize("head_dim,window", [(64, 0), (64, 128), (128, 0), (128, 128)])
+def test_largest_accepted_sequence(head_dim, window, oracle_lib):
+    """One sequence as long as the call accepts at 64 query / 8 KV heads: its query rows,
+    plus one work-group's rows past the end, within 2^31 - 1 bytes (261887 tokens at
+    head_dim 64, 130943 at 128; test_abi pins that one token more is refused).  Every
+    32-bit buffer offset of the query, output and K/V rows reaches its largest value,
+    and without a window the last rows walk the whole sequence.  The first 8 and last 8
+    positions and 16 between, against the oracle's row routine under the gate and the
+    rounding bound: every query head with the window, one per KV head without."""
+    rows_past = 256 if head_dim == 64 else 128
+    L = (2 ** 31 - 1) // (64 * 2 * head_dim) - rows_past
+    wl = workloads.custom([L], 64, 8, window=window, head_dim=head_dim,
+                          softmax_scale=head_dim ** -0.5, seed=43)
+    inp = workloads.make_inputs(wl)
+    say(f"largest sequence L={L} D={head_dim} W={window}")
+    out = run_gpu(inp)
+    pos = np.unique(np.concatenate([np.arange(8), np.arange(L - 8, L),
+                                    np.linspace(8, L - 9, 16).astype(np.int64)]))
+    if window:
+        rows, heads = np.repeat(pos, 64), np.tile(np.arange(64), pos.size)
+    else:
+        rows = np.repeat(pos, 8)
+        heads = np.tile(np.arange(8) * 8, pos.size) + np.repeat(pos % 8, 8)
+    got = f64(out[torch.from_numpy(rows).to(out.device), torch.from_numpy(heads).to(out.device)])
+    del out
+    torch.cuda.synchronize()
+    ref = oracle.prefill_rows(*oracle_args(inp), rows=rows, heads=heads, lib=oracle_lib)
+    check(got, ref, f"L={L} D={head_dim} W={window}")
+    excess = np.abs(got - ref) - rounding_bound(inp, ref, oracle_lib, rows=rows, heads=heads)
+    assert excess.max() <= 0, f"rounding bound exceeded by {excess.max():.3e}"
