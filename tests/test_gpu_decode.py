@@ -219,3 +219,17 @@ def test_decode_head_groups(case, oracle_lib):
     check(got, ref, f"n_seqs={n} G={hq // hkv} D={d} W={w}", bound=cache_rounding_bound(inp, ref, oracle_lib))
     empty = [b for b, L in enumerate(k_lens) if L == 0]
     assert np.all(got[empty] == 0.0), "a sequence without keys must give zero rows"
+
+
+def test_decode_million_keys(oracle_lib):
+    """Sequences of 2^20 and 2^19 + 5 cached keys beside a 3-key one (64 q / 8 KV heads,
+    page 16: 98 306 pages spread at random over the pool): page ids and byte offsets far
+    into a 3 GiB cache, 128 key chunks per sequence merged, against the oracle's cache
+    form under the gate and the rounding bound."""
+    wl = workloads.decode([1 << 20, 3, (1 << 19) + 5], n_q_heads=64, n_kv_heads=8, page_size=16, seed=73)
+    inp = workloads.make_cache_inputs(wl)
+    say("decode 2^20 cached keys")
+    got = f64(run_gpu_decode(inp).cpu())
+    torch.cuda.synchronize()
+    ref = oracle.cache_attend(*cache_oracle_args(inp), lib=oracle_lib)
+    check(got, ref, "2^20 keys", bound=cache_rounding_bound(inp, ref, oracle_lib))
