@@ -15,7 +15,11 @@
 // positions of one sequence.  Every K/V tile it stages in LDS therefore serves
 // the whole head group (the GQA reuse).  The work-group walks the 64-key tiles
 // that intersect its causal (and window) range; tiles entirely visible to all
-// of its rows skip the mask.
+// of its rows skip the mask.  The grid runs the KV head fastest (consecutive
+// work-group ids go to different XCDs, so each XCD's L2 serves fixed heads)
+// and the position blocks last-first, the longest causal walks first, in
+// groups of sequences whose K/V fit one XCD's L2; a ragged pack's blocks past
+// their sequence's end are left out of the order (cdna4.h).
 //
 // Orientation.  Scores are formed transposed, S^T = K Q^T, with
 // v_mfma_f32_32x32x16_bf16.  In that instruction's accumulator layout lane l
