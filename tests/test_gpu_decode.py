@@ -51,6 +51,8 @@ CASES = [
     ([8192], 64, 8, 16, 0, True),                       # one long sequence: 64 chunks
     ([5000, 2, 3001], 4, 4, 64, 0, True),
     ([9000, 130], 16, 1, 16, 1000, True),               # window spanning several chunks
+    ([5000, 17, 2048, 0, 4097], 16, 2, 2048, 0, True),  # pages longer than a key chunk
+    ([5000, 17, 2048, 0, 4097], 32, 8, 1024, 300, True),
 ]
 
 

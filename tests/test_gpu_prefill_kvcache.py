@@ -50,6 +50,8 @@ CASES = [
     (*CHUNKS, 8, 1, 64, 300, True),
     ([0, 3, 0, 7, 1], [10, 3, 0, 700, 1], 16, 2, 16, 0, True),
     ([1, 1, 1], [5000, 17, 64], 16, 2, 16, 0, True),
+    (*CHUNKS, 16, 2, 1024, 0, True),        # pages longer than a key tile or a query block
+    (*CHUNKS, 64, 8, 2048, 100, True),
 ]
 
 
