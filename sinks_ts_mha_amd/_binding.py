@@ -83,11 +83,19 @@ def ts_mha_unmasked_pairs(cu_seqlens, window: int = 0) -> int:
     return int(r)
 
 
-def _overlaps(a: torch.Tensor, b: torch.Tensor) -> bool:
-    a0, b0 = a.data_ptr(), b.data_ptr()
-    a1 = a0 + a.numel() * a.element_size()
-    b1 = b0 + b.numel() * b.element_size()
-    return a0 < b1 and b0 < a1 and a.numel() > 0 and b.numel() > 0
+def _check_no_overlap(out: torch.Tensor, inputs) -> None:
+    """Raise if out's bytes overlap those of any (name, tensor) in inputs (None skipped)."""
+    o0 = out.data_ptr()
+    o1 = o0 + out.numel() * out.element_size()
+    if o1 == o0:
+        return
+    for name, t in inputs:
+        if t is None:
+            continue
+        t0 = t.data_ptr()
+        t1 = t0 + t.numel() * t.element_size()
+        if t0 < o1 and o0 < t1 and t1 > t0:
+            raise ValueError(f"out must not overlap {name}")
 
 
 def ts_mha_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks, cu_seqlens,
@@ -125,10 +133,7 @@ def ts_mha_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks, cu_
     elif out.shape != q.shape or out.dtype != torch.bfloat16 or out.device != dev \
             or not out.is_contiguous():
         raise ValueError("out must be a contiguous bfloat16 tensor shaped like q on q's device")
-    for name, t in (("q", q), ("k", k), ("v", v), ("cu_seqlens", cu_seqlens)) + \
-            ((("sinks", sinks),) if sinks is not None else ()):
-        if _overlaps(out, t):
-            raise ValueError(f"out must not overlap {name}")
+    _check_no_overlap(out, (("q", q), ("k", k), ("v", v), ("cu_seqlens", cu_seqlens), ("sinks", sinks)))
     if softmax_scale is None:
         softmax_scale = 1.0 / (D ** 0.5)
     if T == 0:  # no rows: nothing to compute or write (torch gives empty tensors no address)
@@ -137,9 +142,7 @@ def ts_mha_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks, cu_
     if max_seqlen is None:
         cu = cu_seqlens.cpu()
         max_seqlen = int((cu[1:] - cu[:-1]).max()) if n_seqs > 0 else 0
-    if stream is None:
-        stream = torch.cuda.current_stream(dev)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    handle = _stream_handle(stream, dev)
     rc = lib().ts_mha_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(),
                               None if sinks is None else sinks.data_ptr(),
                               cu_seqlens.data_ptr(), hq, hkv, D, int(window), float(softmax_scale),
@@ -156,8 +159,13 @@ def _check_tensor(name, t, dtype, dim, dev):
         raise ValueError(f"{name} must be a contiguous tensor on {dev}")
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream_handle(stream, dev):
     if stream is None:
+        if _raw_stream is not None:  # the current stream's handle without a Stream object (~2 us less)
+            return _raw_stream(dev.index if dev.index is not None else torch.cuda.current_device())
         stream = torch.cuda.current_stream(dev)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
@@ -188,9 +196,7 @@ def _check_out(out, q, inputs):
         _check_tensor("out", out, torch.bfloat16, 3, q.device)
         if out.shape != q.shape:
             raise ValueError("out must be shaped like q")
-    for name, t in inputs:
-        if t is not None and _overlaps(out, t):
-            raise ValueError(f"out must not overlap {name}")
+    _check_no_overlap(out, inputs)
     return out
 
 

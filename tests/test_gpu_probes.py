@@ -391,3 +391,42 @@ def test_debug_seqlens_validation(monkeypatch):
     assert ei.value.code == -9
     tm.ts_mha_prefill(q, k, k.clone(), None, cu, max_seqlen=5)
     torch.cuda.synchronize()
+
+
+def test_binding_rejects_overlapping_out():
+    """The binding refuses an output that shares bytes with any input (the kernels read the
+    inputs while they write the output), and accepts an adjacent, non-overlapping one."""
+    wl = workloads.custom([64, 64], 16, 2, seed=22)
+    inp = workloads.make_inputs(wl, device="cuda")
+    q, k, v, s, cu = inp["q"], inp["k"], inp["v"], inp["sinks"], inp["cu_seqlens"]
+    say("binding overlap checks")
+    n, bf = q.numel(), torch.bfloat16
+    buf = torch.empty(2 * n, dtype=bf, device="cuda")  # q, then room for an output
+    qq = buf[:n].view(q.shape)
+    qq.copy_(q)
+    with pytest.raises(ValueError, match="overlap"):
+        tm.ts_mha_prefill(qq, k, v, s, cu, out=qq, max_seqlen=64)
+    with pytest.raises(ValueError, match="overlap"):
+        tm.ts_mha_prefill(qq, k, v, s, cu, out=buf[n // 2: n // 2 + n].view(q.shape), max_seqlen=64)
+    kbuf = torch.empty(n, dtype=bf, device="cuda")  # k inside the output's bytes
+    kk = kbuf[: k.numel()].view(k.shape)
+    kk.copy_(k)
+    with pytest.raises(ValueError, match="overlap"):
+        tm.ts_mha_prefill(q, kk, v, s, cu, out=kbuf.view(q.shape), max_seqlen=64)
+    sbuf = torch.empty(n, dtype=bf, device="cuda")  # the sinks inside the output's bytes
+    ss = sbuf[: 2 * s.numel()].view(torch.float32)
+    ss.copy_(s)
+    with pytest.raises(ValueError, match="overlap"):
+        tm.ts_mha_prefill(q, k, v, ss, cu, out=sbuf.view(q.shape), max_seqlen=64)
+    dwl = workloads.decode([40, 7], n_q_heads=16, n_kv_heads=2, page_size=16, seed=23)
+    dinp = workloads.make_cache_inputs(dwl)
+    dq = dinp["q"].cuda()
+    with pytest.raises(ValueError, match="overlap"):
+        tm.ts_mha_decode_with_kvcache(dq, dinp["k_cache"].cuda(), dinp["v_cache"].cuda(), dinp["sinks"].cuda(),
+                                      dinp["seqlens_k"].cuda(), dinp["block_table"].cuda(), out=dq,
+                                      max_seqlen_k=dwl.max_seqlen_k)
+    out = buf[n:].view(q.shape)  # adjacent to q, not overlapping
+    tm.ts_mha_prefill(qq, k, v, s, cu, out=out, max_seqlen=64)
+    ref = tm.ts_mha_prefill(q, k, v, s, cu, max_seqlen=64)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
