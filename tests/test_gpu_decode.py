@@ -51,6 +51,9 @@ CASES = [
     ([8192], 64, 8, 16, 0, True),                       # one long sequence: 64 chunks
     ([5000, 2, 3001], 4, 4, 64, 0, True),
     ([9000, 130], 16, 1, 16, 1000, True),               # window spanning several chunks
+    (EDGES, 1, 1, 16, 0, True),            # a single head
+    (EDGES, 64, 64, 16, 0, True),          # 64 KV heads, G = 1: two per work-group
+    (EDGES, 128, 8, 32, 100, True),        # 128 query heads, G = 16
     ([5000, 17, 2048, 0, 4097], 16, 2, 2048, 0, True),  # pages longer than a key chunk
     ([5000, 17, 2048, 0, 4097], 32, 8, 1024, 300, True),
 ]

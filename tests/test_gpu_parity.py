@@ -45,6 +45,10 @@ SMALL_CASES = [
     ([0, 1, 0, 5, 1, 0, 70], 16, 2, 0, True),
     ([1000], 64, 8, 0, True),
     ([777, 1], 32, 2, 64, True),
+    (RAGGED, 1, 1, 0, True),       # a single head
+    (RAGGED, 2, 1, 100, True),
+    (RAGGED, 64, 64, 0, True),     # 64 KV heads (8 per XCD), G = 1
+    (RAGGED, 128, 8, 129, True),   # 128 query heads, G = 16
 ]
 
 
