@@ -195,6 +195,9 @@ HEAD_GROUP_CASES = [
     ((256, 150, 0.2), 16, 2, 128, 100),
     ((4, 9000, 0.25), 32, 4, 64, 2500),   # long windowed spans: 4 heads and split chunks
     ((3, 6000, 0.0), 8, 8, 128, 0),       # head_dim 128, G = 1: 2 heads and split chunks
+    ((3, 5000, 0.0), 8, 4, 64, 0),        # 4 heads of G = 2, split chunks
+    ((3, 5000, 0.0), 16, 4, 64, 3000),    # 4 heads of G = 4, a window over several chunks
+    ((4, 9000, 0.0), 64, 4, 64, 0),       # 4 heads of G = 16
 ]
 
 
